@@ -1,0 +1,348 @@
+// api.hip -- the exported C ABI (include/mlora.h): adapter pool, workspace,
+// host-side validation and kernel dispatch. Host code only.
+#include <hip/hip_runtime.h>
+
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "../../include/mlora.h"
+#include "launch.h"
+
+using namespace mlora;
+
+struct mlora_pool_s {
+  void* base = nullptr;
+  size_t bytes = 0;
+  int d_in = 0, d_out = 0, dtype = 0, max_rank = 0, capacity = 0;
+  size_t elem = 0;
+  long long slot_elems = 0;  // elements per slot (multiple of 128)
+  long long b_offset = 0;    // elements from slot start to B
+  int32_t* dev_rank = nullptr;
+  std::vector<int> host_rank;
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+size_t elem_size(int dtype) { return dtype == MLORA_F32 ? 4 : dtype == MLORA_BF16 ? 2 : 0; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Slot geometry: A [max_rank, d_in] then B [d_out, round_up8(max_rank)].
+void slot_geometry(int d_in, int d_out, int max_rank, long long* slot_elems, long long* b_off) {
+  const long long a_elems = (long long)max_rank * d_in;
+  const long long b_elems = (long long)d_out * ((max_rank + 7) & ~7);
+  *b_off = (a_elems + 127) / 128 * 128;
+  *slot_elems = (*b_off + b_elems + 127) / 128 * 128;
+}
+
+bool shape_ok(int d_in, int d_out, int dtype, int max_rank, int capacity) {
+  if (elem_size(dtype) == 0) return false;
+  if (d_in < 1 || d_in > MLORA_MAX_DIM || d_out < 1 || d_out > MLORA_MAX_DIM) return false;
+  if (d_in % (dtype == MLORA_F32 ? 4 : 8) != 0) return false;
+  if (max_rank < 1 || max_rank > MLORA_MAX_RANK) return false;
+  if (capacity < 1 || capacity > (1 << 20)) return false;
+  return true;
+}
+
+// Workspace layout for up to T tokens.
+struct WsLayout {
+  size_t err, token_index, seg_start, seg_adapter, seg_rank, seg_scale, n_seg, counts, v_part, total;
+};
+
+int r_ws_of(int max_rank) { return (max_rank + 15) / 16 * 16; }
+
+WsLayout ws_layout(const mlora_pool_s* p, int T) {
+  WsLayout L;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes, kAlign); return at; };
+  const size_t t1 = (size_t)T + 2;
+  L.err = take(16);
+  L.token_index = take(t1 * 4);
+  L.seg_start = take(t1 * 4);
+  L.seg_adapter = take(t1 * 4);
+  L.seg_rank = take(t1 * 4);
+  L.seg_scale = take(t1 * 4);
+  L.n_seg = take(16);
+  L.counts = take(t1 * 4);
+  L.v_part = take((size_t)kMaxShrinkSplit * T * r_ws_of(p->max_rank) * 4);
+  L.total = o;
+  return L;
+}
+
+PoolView view_of(const mlora_pool_s* p) {
+  PoolView v;
+  v.base = p->base;
+  v.rank = p->dev_rank;
+  v.slot_elems = p->slot_elems;
+  v.b_offset = p->b_offset;
+  v.capacity = p->capacity;
+  v.max_rank = p->max_rank;
+  return v;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MLORA_OK : MLORA_ERR_HIP; }
+
+int check_launch() { return hip_status(hipGetLastError()); }
+
+// Launch the layer on sorted metadata already resident on the device.
+int run_linear(const void* x, const void* W, mlora_pool_s* pool, const SegView& sv, int T,
+               int lora_on, void* y, char* ws, hipStream_t stream) {
+  const WsLayout L = ws_layout(pool, T);
+  LinearArgs a;
+  a.x = x;
+  a.W = W;
+  a.y = y;
+  a.T = T;
+  a.d_in = pool->d_in;
+  a.d_out = pool->d_out;
+  a.lora_on = lora_on;
+  a.sv = sv;
+  a.pv = view_of(pool);
+  a.v_part = (float*)(ws + L.v_part);
+  a.r_ws = r_ws_of(pool->max_rank);
+  a.seg_grid = lora_on ? sv.n_seg : 0;
+  if (pool->dtype == MLORA_BF16) {
+    a.ks = choose_shrink_split_bf16(pool->d_in, a.seg_grid);
+    launch_linear_bf16(a, stream);
+  } else {
+    a.ks = 1;
+    launch_linear_f32(a, stream);
+  }
+  return check_launch();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mlora_status_string(int status) {
+  switch (status) {
+    case MLORA_OK: return "ok";
+    case MLORA_ERR_INVALID_ARG: return "invalid argument";
+    case MLORA_ERR_SHAPE: return "unsupported shape";
+    case MLORA_ERR_DTYPE: return "unsupported dtype";
+    case MLORA_ERR_RANK: return "bad adapter rank";
+    case MLORA_ERR_ADAPTER: return "adapter id out of range or not registered";
+    case MLORA_ERR_EXISTS: return "adapter id already registered";
+    case MLORA_ERR_WORKSPACE: return "workspace or pool arena too small";
+    case MLORA_ERR_METADATA: return "inconsistent segment metadata";
+    case MLORA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+size_t mlora_pool_bytes(int d_in, int d_out, int dtype, int max_rank, int capacity) {
+  if (!shape_ok(d_in, d_out, dtype, max_rank, capacity)) return 0;
+  long long se, bo;
+  slot_geometry(d_in, d_out, max_rank, &se, &bo);
+  const size_t slots = align_up((size_t)capacity * (size_t)se * elem_size(dtype), kAlign);
+  return slots + align_up((size_t)capacity * 4, kAlign);
+}
+
+int mlora_pool_create(void* dev_mem, size_t bytes, int d_in, int d_out, int dtype, int max_rank,
+                      int capacity, hipStream_t stream, mlora_pool_t* out) {
+  if (!out || !dev_mem || !aligned16(dev_mem)) return MLORA_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (elem_size(dtype) == 0) return MLORA_ERR_DTYPE;
+  if (!shape_ok(d_in, d_out, dtype, max_rank, capacity)) return MLORA_ERR_SHAPE;
+  const size_t need = mlora_pool_bytes(d_in, d_out, dtype, max_rank, capacity);
+  if (bytes < need) return MLORA_ERR_WORKSPACE;
+  mlora_pool_s* p = new (std::nothrow) mlora_pool_s();
+  if (!p) return MLORA_ERR_INVALID_ARG;
+  p->base = dev_mem;
+  p->bytes = bytes;
+  p->d_in = d_in;
+  p->d_out = d_out;
+  p->dtype = dtype;
+  p->max_rank = max_rank;
+  p->capacity = capacity;
+  p->elem = elem_size(dtype);
+  slot_geometry(d_in, d_out, max_rank, &p->slot_elems, &p->b_offset);
+  const size_t slots = align_up((size_t)capacity * (size_t)p->slot_elems * p->elem, kAlign);
+  p->dev_rank = (int32_t*)((char*)dev_mem + slots);
+  p->host_rank.assign(capacity, 0);
+  launch_fill_u32(p->dev_rank, (size_t)capacity, 0u, stream);
+  const int st = check_launch();
+  if (st != MLORA_OK) {
+    delete p;
+    return st;
+  }
+  *out = p;
+  return MLORA_OK;
+}
+
+int mlora_pool_destroy(mlora_pool_t pool) {
+  delete pool;
+  return MLORA_OK;
+}
+
+int mlora_register_adapter(mlora_pool_t p, int adapter_id, int rank, const void* A, const void* B,
+                           hipStream_t stream) {
+  if (!p || !A || !B) return MLORA_ERR_INVALID_ARG;
+  if (adapter_id < 0 || adapter_id >= p->capacity) return MLORA_ERR_ADAPTER;
+  if (rank < 1 || rank > p->max_rank) return MLORA_ERR_RANK;
+  if (p->host_rank[adapter_id] != 0) return MLORA_ERR_EXISTS;
+  char* slot = (char*)p->base + (size_t)adapter_id * (size_t)p->slot_elems * p->elem;
+  // A: [rank, d_in] contiguous
+  hipError_t e = hipMemcpyAsync(slot, A, (size_t)rank * p->d_in * p->elem, hipMemcpyDefault, stream);
+  if (e != hipSuccess) return MLORA_ERR_HIP;
+  // B: [d_out, rank] -> rows padded to round_up8(rank) with zeros
+  char* bdst = slot + (size_t)p->b_offset * p->elem;
+  const int bld = (rank + 7) & ~7;
+  if (bld != rank) {
+    const size_t words = (size_t)p->d_out * bld * p->elem / 4;
+    launch_fill_u32(bdst, words, 0u, stream);
+    if (check_launch() != MLORA_OK) return MLORA_ERR_HIP;
+  }
+  e = hipMemcpy2DAsync(bdst, (size_t)bld * p->elem, B, (size_t)rank * p->elem, (size_t)rank * p->elem,
+                       (size_t)p->d_out, hipMemcpyDefault, stream);
+  if (e != hipSuccess) return MLORA_ERR_HIP;
+  launch_set_slot_rank(p->dev_rank, adapter_id, rank, stream);
+  if (check_launch() != MLORA_OK) return MLORA_ERR_HIP;
+  p->host_rank[adapter_id] = rank;
+  return MLORA_OK;
+}
+
+int mlora_unregister_adapter(mlora_pool_t p, int adapter_id, hipStream_t stream) {
+  if (!p) return MLORA_ERR_INVALID_ARG;
+  if (adapter_id < 0 || adapter_id >= p->capacity) return MLORA_ERR_ADAPTER;
+  if (p->host_rank[adapter_id] == 0) return MLORA_ERR_ADAPTER;
+  launch_set_slot_rank(p->dev_rank, adapter_id, 0, stream);
+  if (check_launch() != MLORA_OK) return MLORA_ERR_HIP;
+  p->host_rank[adapter_id] = 0;
+  return MLORA_OK;
+}
+
+int mlora_adapter_rank(mlora_pool_t p, int adapter_id) {
+  if (!p || adapter_id < 0 || adapter_id >= p->capacity) return -1;
+  return p->host_rank[adapter_id];
+}
+
+size_t mlora_workspace_bytes(mlora_pool_t p, int max_tokens) {
+  if (!p || max_tokens < 0 || max_tokens > MLORA_MAX_TOKENS) return 0;
+  return ws_layout(p, max_tokens).total;
+}
+
+int mlora_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!workspace || !aligned16(workspace)) return MLORA_ERR_INVALID_ARG;
+  launch_fill_u32(workspace, workspace_bytes / 4, 0u, stream);
+  return check_launch();
+}
+
+int mlora_linear(const void* x, const void* W, mlora_pool_t pool, const int32_t* seg_start,
+                 const int32_t* seg_adapter, const int32_t* seg_rank, const float* seg_scale,
+                 const int32_t* token_index, int n_tokens, int n_seg, int lora_on, void* y,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!pool) return MLORA_ERR_INVALID_ARG;
+  if (lora_on != 0 && lora_on != 1) return MLORA_ERR_INVALID_ARG;
+  if (n_tokens < 0 || n_tokens > MLORA_MAX_TOKENS) return MLORA_ERR_SHAPE;
+  if (n_tokens == 0) return MLORA_OK;
+  if (!x || !W || !y || !workspace) return MLORA_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(W) || !aligned16(y) || !aligned16(workspace))
+    return MLORA_ERR_INVALID_ARG;
+  if (workspace_bytes < ws_layout(pool, n_tokens).total) return MLORA_ERR_WORKSPACE;
+  SegView sv{};
+  if (lora_on) {
+    if (!seg_start || !seg_adapter || !seg_rank || !seg_scale) return MLORA_ERR_INVALID_ARG;
+    if (n_seg < 1 || n_seg > n_tokens + pool->capacity + 1) return MLORA_ERR_METADATA;
+    sv.seg_start = seg_start;
+    sv.seg_adapter = seg_adapter;
+    sv.seg_rank = seg_rank;
+    sv.seg_scale = seg_scale;
+    sv.token_index = token_index;
+    sv.n_seg_dev = nullptr;
+    sv.n_seg = n_seg;
+  }
+  return run_linear(x, W, pool, sv, n_tokens, lora_on, y, (char*)workspace, stream);
+}
+
+int mlora_build_segments(const int32_t* token_adapter, const float* adapter_scale, int n_tokens,
+                         mlora_pool_t pool, int32_t* token_index, int32_t* seg_start,
+                         int32_t* seg_adapter, int32_t* seg_rank, float* seg_scale,
+                         int32_t* n_seg_out, hipStream_t stream) {
+  if (!pool || !seg_start || !n_seg_out) return MLORA_ERR_INVALID_ARG;
+  if (n_tokens < 0 || n_tokens > MLORA_MAX_UNSORTED_TOKENS) return MLORA_ERR_SHAPE;
+  if (n_tokens > 0 && (!token_adapter || !adapter_scale || !token_index || !seg_adapter ||
+                       !seg_rank || !seg_scale))
+    return MLORA_ERR_INVALID_ARG;
+  launch_build_segments(token_adapter, adapter_scale, n_tokens, view_of(pool), token_index,
+                        seg_start, seg_adapter, seg_rank, seg_scale, n_seg_out, stream);
+  return check_launch();
+}
+
+int mlora_linear_tokens(const void* x, const void* W, mlora_pool_t pool,
+                        const int32_t* token_adapter, const float* adapter_scale, int n_tokens,
+                        int lora_on, void* y, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+  if (!pool) return MLORA_ERR_INVALID_ARG;
+  if (lora_on != 0 && lora_on != 1) return MLORA_ERR_INVALID_ARG;
+  if (n_tokens < 0 || n_tokens > MLORA_MAX_UNSORTED_TOKENS) return MLORA_ERR_SHAPE;
+  if (n_tokens == 0) return MLORA_OK;
+  if (!x || !W || !y || !workspace) return MLORA_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(W) || !aligned16(y) || !aligned16(workspace))
+    return MLORA_ERR_INVALID_ARG;
+  const WsLayout L = ws_layout(pool, n_tokens);
+  if (workspace_bytes < L.total) return MLORA_ERR_WORKSPACE;
+  SegView sv{};
+  if (lora_on) {
+    if (!token_adapter || !adapter_scale) return MLORA_ERR_INVALID_ARG;
+    char* ws = (char*)workspace;
+    int32_t* ti = (int32_t*)(ws + L.token_index);
+    int32_t* ss = (int32_t*)(ws + L.seg_start);
+    int32_t* sa = (int32_t*)(ws + L.seg_adapter);
+    int32_t* sr = (int32_t*)(ws + L.seg_rank);
+    float* sc = (float*)(ws + L.seg_scale);
+    int32_t* ns = (int32_t*)(ws + L.n_seg);
+    launch_build_segments(token_adapter, adapter_scale, n_tokens, view_of(pool), ti, ss, sa, sr,
+                          sc, ns, stream);
+    const int st = check_launch();
+    if (st != MLORA_OK) return st;
+    sv.seg_start = ss;
+    sv.seg_adapter = sa;
+    sv.seg_rank = sr;
+    sv.seg_scale = sc;
+    sv.token_index = ti;
+    sv.n_seg_dev = ns;
+    sv.n_seg = n_tokens;  // upper bound on the device count
+  }
+  return run_linear(x, W, pool, sv, n_tokens, lora_on, y, (char*)workspace, stream);
+}
+
+int mlora_token_map(const int32_t* seg_start, const int32_t* seg_adapter, int n_tokens, int n_seg,
+                    int32_t* token_seg, int32_t* token_adapter_out, hipStream_t stream) {
+  if (n_tokens < 0 || n_seg < 0) return MLORA_ERR_SHAPE;
+  if (n_tokens == 0) return MLORA_OK;
+  if (!seg_start || (n_seg > 0 && !seg_adapter) || !token_seg || !token_adapter_out)
+    return MLORA_ERR_INVALID_ARG;
+  launch_token_map(seg_start, seg_adapter, n_tokens, n_seg, token_seg, token_adapter_out, stream);
+  return check_launch();
+}
+
+int mlora_validate(mlora_pool_t pool, const int32_t* seg_start, const int32_t* seg_adapter,
+                   const int32_t* seg_rank, const int32_t* token_index, int n_tokens, int n_seg,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!pool || !seg_start || !workspace) return MLORA_ERR_INVALID_ARG;
+  if (n_tokens < 0 || n_seg < 0 || n_tokens > MLORA_MAX_TOKENS) return MLORA_ERR_SHAPE;
+  if (n_seg > 0 && !seg_adapter) return MLORA_ERR_INVALID_ARG;
+  const WsLayout L = ws_layout(pool, n_tokens);
+  if (workspace_bytes < L.total) return MLORA_ERR_WORKSPACE;
+  char* ws = (char*)workspace;
+  int32_t* result = (int32_t*)(ws + L.err);
+  launch_validate(seg_start, seg_adapter, seg_rank, token_index, n_tokens, n_seg, view_of(pool),
+                  (int32_t*)(ws + L.counts), result, stream);
+  int st = check_launch();
+  if (st != MLORA_OK) return st;
+  int32_t host = -1;
+  if (hipMemcpyAsync(&host, result, sizeof(host), hipMemcpyDeviceToHost, stream) != hipSuccess)
+    return MLORA_ERR_HIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return MLORA_ERR_HIP;
+  return host;
+}
+
+}  // extern "C"

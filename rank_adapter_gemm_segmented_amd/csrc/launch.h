@@ -1,0 +1,50 @@
+// launch.h -- host-side launchers of the gfx950 kernels (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/mlora.h"
+#include "common.h"
+
+namespace mlora {
+
+// Arguments of one layer call after host validation.
+struct LinearArgs {
+  const void* x;
+  const void* W;
+  void* y;
+  int T, d_in, d_out;
+  int lora_on;
+  SegView sv;
+  PoolView pv;
+  float* v_part;   // workspace: shrink partials [ks][T][r_ws] fp32
+  int r_ws;        // row pitch of v_part (max_rank rounded up to 16)
+  int ks;          // number of d_in chunks of the shrink (1..kMaxShrinkSplit)
+  int seg_grid;    // number of segments to cover (upper bound)
+};
+
+constexpr int kMaxShrinkSplit = 16;
+
+// metadata kernels (kernels_meta.hip)
+void launch_token_map(const int32_t* seg_start, const int32_t* seg_adapter, int T, int S,
+                      int32_t* token_seg, int32_t* token_adapter, hipStream_t st);
+size_t build_segments_lds_bytes(int T);
+void launch_build_segments(const int32_t* token_adapter, const float* adapter_scale, int T,
+                           const PoolView& pv, int32_t* token_index, int32_t* seg_start,
+                           int32_t* seg_adapter, int32_t* seg_rank, float* seg_scale,
+                           int32_t* n_seg_out, hipStream_t st);
+void launch_validate(const int32_t* seg_start, const int32_t* seg_adapter, const int32_t* seg_rank,
+                     const int32_t* token_index, int T, int S, const PoolView& pv, int32_t* counts,
+                     int32_t* result, hipStream_t st);
+void launch_fill_u32(void* p, size_t n_words, uint32_t v, hipStream_t st);
+void launch_set_slot_rank(int32_t* table, int id, int rank, hipStream_t st);
+
+// bf16 path (kernels_bf16.hip)
+void launch_linear_bf16(const LinearArgs& a, hipStream_t st);
+int choose_shrink_split_bf16(int d_in, int seg_grid);
+
+// fp32 path (kernels_f32.hip)
+void launch_linear_f32(const LinearArgs& a, hipStream_t st);
+
+}  // namespace mlora

@@ -1,0 +1,158 @@
+"""GPU invariants that hold bit for bit, and the library's error paths.
+
+* lora_on = 1 with every B = 0 equals lora_on = 0 (the adapter term vanishes;
+  the base accumulation order does not depend on lora_on).
+* Permuting the batch (rows with their adapter ids) permutes y exactly: no
+  token's arithmetic depends on where it sits in a tile.
+* Two runs give identical bits (no atomics in any reduction).
+* Metadata checks on the device agree with the oracle's error semantics.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import DeviceCase, compare, f32, i32, log, to_dev, y_host
+from mlora_inputs import Adapter, make_case, make_custom_case
+
+pytestmark = pytest.mark.gpu
+
+
+def _ml():
+    import rank_adapter_gemm_segmented_amd as ml
+    return ml
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_zero_B_equals_lora_off(dtype):
+    log(f"[invariant] B=0 equals lora_off ({dtype})")
+    ids = sorted(np.random.default_rng(1).integers(0, 6, size=70).tolist())
+    c = make_custom_case(31, dtype, 512, 384, ids, {a: [8, 16, 32, 64, 4, 12][a] for a in range(6)})
+    for ad in c.adapters.values():
+        ad.B[:] = 0
+    dc = DeviceCase(c)
+    y_on = dc.run(1).clone()
+    y_off = dc.run(0).clone()
+    assert torch.equal(y_on.view(torch.int16) if dtype == "bf16" else y_on.view(torch.int32),
+                       y_off.view(torch.int16) if dtype == "bf16" else y_off.view(torch.int32))
+
+
+def test_permutation_bitwise():
+    log("[invariant] permutation")
+    rng = np.random.default_rng(2)
+    T = 150
+    ids = rng.integers(-1, 20, size=T).tolist()
+    ranks = {a: [8, 16, 32, 64][a % 4] for a in range(20)}
+    c = make_custom_case(41, "bf16", 1024, 640, ids, ranks, sorted_input=False)
+    dc = DeviceCase(c)
+    ml = _ml()
+    y = dc.run(1).clone()
+    perm = rng.permutation(T)
+    xp = dc.x[torch.from_numpy(perm).cuda()].contiguous()
+    tp = i32(np.asarray(ids, np.int32)[perm])
+    yp = ml.linear_tokens(xp, dc.W, dc.pool, tp, dc.adapter_scale, lora_on=1, workspace=dc.ws)
+    torch.cuda.synchronize()
+    assert torch.equal(yp.view(torch.int16), y[torch.from_numpy(perm).cuda()].view(torch.int16))
+
+
+@pytest.mark.parametrize("name", ["decode_bf16", "hetero_bf16"])
+def test_run_to_run_determinism(name):
+    log(f"[invariant] determinism {name}")
+    dc = DeviceCase(make_case(name))
+    y1 = dc.run(1).clone()
+    y2 = dc.run(1).clone()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+def test_sorted_and_unsorted_paths_agree():
+    # the same batch given pre-grouped (sorted metadata) or unsorted (library
+    # segments it) yields the same bits
+    log("[invariant] sorted vs unsorted")
+    rng = np.random.default_rng(3)
+    ids = rng.integers(-1, 10, size=90)
+    ranks = {a: [8, 16, 32][a % 3] for a in range(10)}
+    cu = make_custom_case(51, "bf16", 768, 512, ids.tolist(), ranks, sorted_input=False)
+    dc = DeviceCase(cu)
+    y_u = y_host(dc.run(1))
+    ti, ss, sa = oracle.segment(cu.token_adapter, cu.capacity)
+    sr = np.array([ranks[a] if a >= 0 else 0 for a in sa], np.int32)
+    sc = np.array([cu.adapter_scale[a] if a >= 0 else 0 for a in sa], np.float32)
+    ml = _ml()
+    y_s = ml.linear(dc.x, dc.W, dc.pool, i32(ss), i32(sa), i32(sr), f32(sc), lora_on=1,
+                    token_index=i32(ti), workspace=dc.ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(y_host(y_s), y_u)
+
+
+def test_validate_matches_oracle_errors():
+    log("[invariant] validate")
+    ml = _ml()
+    c = make_custom_case(61, "bf16", 64, 64, [0, 0, 1, 1], {0: 8, 1: 16}, capacity=4)
+    dc = DeviceCase(c)
+    pool = oracle.PackedPool(c.adapters, c.capacity, 64, 64)
+
+    def both(ss, sa, sr, ti=None):
+        g = ml.validate(dc.pool, i32(ss), i32(sa), i32(sr), None if ti is None else i32(ti),
+                        n_tokens=4, workspace=dc.ws)
+        try:
+            oracle.linear(c.x, c.W, pool, np.array(ss, np.int32), np.array(sa, np.int32),
+                          np.array(sr, np.int32), np.ones(len(sa), np.float32),
+                          None if ti is None else np.array(ti, np.int32), 1)
+            o = 0
+        except oracle.OracleError as e:
+            o = {oracle.MLO_ERR_META: 8, oracle.MLO_ERR_ADAPTER: 5, oracle.MLO_ERR_RANK: 4}[e.code]
+        return g, o
+
+    for args in [([0, 2, 4], [0, 1], [8, 16]),
+                 ([0, 2, 3], [0, 1], [8, 16]),
+                 ([0, 3, 2, 4], [0, 1, 1], [8, 16, 16]),
+                 ([0, 2, 4], [0, 3], [8, 16]),          # slot 3 not registered
+                 ([0, 2, 4], [0, 9], [8, 16]),          # beyond capacity
+                 ([0, 2, 4], [0, 1], [8, 8]),           # rank mismatch
+                 ([0, 2, 4], [-1, 1], [0, 16]),
+                 ([0, 2, 4], [0, 1], [8, 16], [1, 0, 3, 2]),
+                 ([0, 2, 4], [0, 1], [8, 16], [1, 1, 3, 2])]:
+        g, o = both(*args)
+        assert g == o, (args, g, o)
+
+
+def test_host_validation_errors():
+    ml = _ml()
+    c = make_custom_case(71, "bf16", 64, 64, [0, 0], {0: 8})
+    dc = DeviceCase(c)
+    E = ml.STATUS_CODE
+    with pytest.raises(ml.MloraError) as e:
+        ml.linear(dc.x, dc.W, dc.pool, dc.seg_start, dc.seg_adapter, dc.seg_rank, dc.seg_scale,
+                  lora_on=2, workspace=dc.ws)
+    assert e.value.code == E["MLORA_ERR_INVALID_ARG"]
+    with pytest.raises(ml.MloraError) as e:
+        ml.linear(dc.x, dc.W, dc.pool, None, None, None, None, lora_on=1, workspace=dc.ws)
+    assert e.value.code == E["MLORA_ERR_INVALID_ARG"]
+    with pytest.raises(ml.MloraError) as e:
+        ml.linear(dc.x, dc.W, dc.pool, dc.seg_start, dc.seg_adapter, dc.seg_rank, dc.seg_scale,
+                  lora_on=1, workspace=dc.ws[:64])
+    assert e.value.code == E["MLORA_ERR_WORKSPACE"]
+    # registration errors
+    A = to_dev(c.adapters[0].A, "bf16")
+    B = to_dev(c.adapters[0].B, "bf16")
+    with pytest.raises(ml.MloraError) as e:
+        dc.pool.register(0, A, B)
+    assert e.value.code == E["MLORA_ERR_EXISTS"]
+    with pytest.raises(ml.MloraError) as e:
+        dc.pool.register(5, A, B)
+    assert e.value.code == E["MLORA_ERR_ADAPTER"]
+    assert dc.pool.rank(0) == 8
+    dc.pool.unregister(0)
+    assert dc.pool.rank(0) == 0
+    with pytest.raises(ml.MloraError) as e:
+        dc.pool.unregister(0)
+    assert e.value.code == E["MLORA_ERR_ADAPTER"]
+    # an unregistered adapter is reported by validate and contributes no term
+    assert ml.validate(dc.pool, dc.seg_start, dc.seg_adapter, dc.seg_rank, n_tokens=2,
+                       workspace=dc.ws) == E["MLORA_ERR_ADAPTER"]
+    y_on = dc.run(1).clone()
+    y_off = dc.run(0).clone()
+    assert torch.equal(y_on.view(torch.int16), y_off.view(torch.int16))
+    # re-register after unregister (hot swap)
+    dc.pool.register(0, A, B)
+    assert dc.pool.rank(0) == 8

@@ -1,0 +1,163 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle on the
+same seeded inputs, element by element.
+
+Tolerances: bf16 outputs |y - y_ref| <= 2e-2 (1 + |y_ref|); fp32 outputs
+|y - y_ref| <= 1e-4 (1 + |y_ref|). Integer outputs (segmentation, token map)
+are compared bit for bit.
+
+Workloads at full size: every row where the oracle takes seconds, otherwise
+the first and last row of every segment plus seeded random rows, computed by
+the oracle one by one.
+"""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import (DeviceCase, check_case, compare, i32, f32, log, oracle_threads,
+                      sample_rows, y_host)
+from mlora_inputs import PREFILL_SHAPES, make_case, make_custom_case
+
+pytestmark = pytest.mark.gpu
+
+
+@functools.lru_cache(maxsize=2)
+def _dev(name, proj="q"):
+    log(f"[parity] building {name} {proj}")
+    return DeviceCase(make_case(name, proj))
+
+
+@pytest.mark.parametrize("lora_on", [0, 1])
+def test_tiny_f32(lora_on):
+    log(f"[parity] tiny_f32 lora_on={lora_on}")
+    check_case(_dev("tiny_f32"), lora_on)
+
+
+@pytest.mark.parametrize("lora_on", [0, 1])
+def test_decode_bf16(lora_on):
+    log(f"[parity] decode_bf16 lora_on={lora_on}")
+    check_case(_dev("decode_bf16"), lora_on)
+
+
+@pytest.mark.parametrize("lora_on", [0, 1])
+def test_verify_bf16(lora_on):
+    log(f"[parity] verify_bf16 lora_on={lora_on}")
+    dc = _dev("verify_bf16")
+    rows = np.arange(0, dc.case.n_tokens, 2, dtype=np.int32)   # first token of each request
+    rows = np.concatenate([rows, [dc.case.n_tokens - 1]]).astype(np.int32)
+    check_case(dc, lora_on, rows)
+
+
+def test_hetero_bf16_unsorted():
+    log("[parity] hetero_bf16 (unsorted ids, library segments)")
+    dc = _dev("hetero_bf16")
+    c = dc.case
+    check_case(dc, 1, sample_rows(c, 48))
+    check_case(dc, 0, sample_rows(c, 16, seed=1))
+    # integer outputs of the segmentation, bit for bit against the oracle
+    import rank_adapter_gemm_segmented_amd as ml
+    ti, ss, sa, sr, sc, ns = ml.build_segments(dc.token_adapter, dc.adapter_scale, dc.pool)
+    torch.cuda.synchronize()
+    o_ti, o_ss, o_sa = oracle.segment(c.token_adapter, c.capacity)
+    S = int(ns.item())
+    assert S == len(o_sa)
+    assert np.array_equal(ti.cpu().numpy(), o_ti)
+    assert np.array_equal(ss[:S + 1].cpu().numpy(), o_ss)
+    assert np.array_equal(sa[:S].cpu().numpy(), o_sa)
+    assert np.array_equal(sr[:S].cpu().numpy(), np.array([c.adapters[a].rank for a in o_sa]))
+    assert np.array_equal(sc[:S].cpu().numpy(), c.adapter_scale[o_sa])
+    # token map of the canonical segments
+    ts, ta = ml.token_map(ss[:S + 1].contiguous(), sa[:S].contiguous(), c.n_tokens)
+    o_ts, o_ta = oracle.token_map(o_ss, o_sa, c.n_tokens)
+    assert np.array_equal(ts.cpu().numpy(), o_ts)
+    assert np.array_equal(ta.cpu().numpy(), o_ta)
+
+
+@pytest.mark.parametrize("proj", list(PREFILL_SHAPES))
+def test_prefill_bf16(proj):
+    log(f"[parity] prefill_bf16 {proj}")
+    dc = _dev("prefill_bf16", proj)
+    check_case(dc, 1, sample_rows(dc.case, 32))
+    check_case(dc, 0, sample_rows(dc.case, 8, seed=2))
+
+
+def test_decode_token_map_bit_exact():
+    dc = _dev("decode_bf16")
+    import rank_adapter_gemm_segmented_amd as ml
+    ts, ta = ml.token_map(dc.seg_start, dc.seg_adapter, dc.case.n_tokens)
+    o_ts, o_ta = oracle.token_map(dc.case.seg_start, dc.case.seg_adapter, dc.case.n_tokens)
+    assert np.array_equal(ts.cpu().numpy(), o_ts)
+    assert np.array_equal(ta.cpu().numpy(), o_ta)
+
+
+# ---------------------------------------------------------------------------
+# small edge cases, every row against the oracle
+# ---------------------------------------------------------------------------
+
+def _edge_cases():
+    cases = []
+    # (seed, dtype, d_in, d_out, ids, ranks, scales, sorted)
+    cases.append((1, "bf16", 64, 64, [0], {0: 16}, None, True))                       # T = 1
+    cases.append((2, "bf16", 72, 17, [0, 0, 1, 1, 1], {0: 3, 1: 7}, {0: -1.0, 1: 0.5}, True))
+    cases.append((3, "bf16", 128, 1000, [-1, -1, 0, 2, 2, 2], {0: 1, 2: 8}, None, True))
+    cases.append((4, "bf16", 4104, 96, list(range(17)), {a: 16 for a in range(17)}, None, True))
+    cases.append((5, "bf16", 256, 320, [0] * 40 + [1] * 25, {0: 64, 1: 32}, {0: 0.0, 1: 2.0}, True))
+    cases.append((6, "bf16", 512, 200, sorted(np.random.default_rng(6).integers(-1, 9, size=300).tolist()),
+                  {a: [8, 16, 32, 64, 1, 3, 7, 24, 40][a] for a in range(9)}, None, True))
+    cases.append((7, "bf16", 256, 130, np.random.default_rng(7).integers(-1, 12, size=77).tolist(),
+                  {a: [8, 16, 32, 64][a % 4] for a in range(12)}, None, False))
+    cases.append((8, "f32", 64, 48, [0, 0, 1, -1, 1, 1, 2], {0: 2, 1: 5, 2: 3}, {0: 1.5, 1: -2.0, 2: 0.25}, True))
+    cases.append((9, "f32", 256, 256, np.random.default_rng(9).integers(-1, 4, size=33).tolist(),
+                  {0: 8, 1: 8, 2: 4, 3: 1}, None, False))
+    cases.append((10, "bf16", 64, 64, [0, 1], {0: 256, 1: 100}, None, True))          # large ranks
+    return cases
+
+
+@pytest.mark.parametrize("idx", range(len(_edge_cases())))
+def test_edge_case(idx):
+    seed, dtype, d_in, d_out, ids, ranks, scales, srt = _edge_cases()[idx]
+    log(f"[parity] edge case {idx}: {dtype} {d_in}->{d_out} T={len(ids)} sorted={srt}")
+    c = make_custom_case(seed, dtype, d_in, d_out, ids, ranks, scales=scales, sorted_input=srt)
+    dc = DeviceCase(c)
+    check_case(dc, 1)
+    check_case(dc, 0)
+
+
+def test_empty_segments_and_base_only_segments():
+    # explicit empty segments inside sorted metadata
+    c = make_custom_case(21, "bf16", 128, 64, [0, 0, 1, 1, 1, 2], {0: 16, 1: 8, 2: 4})
+    dc = DeviceCase(c)
+    ss = np.array([0, 0, 2, 2, 5, 5, 6], np.int32)
+    sa = np.array([1, 0, 2, 1, -1, 2], np.int32)
+    sr = np.array([8, 16, 4, 8, 0, 4], np.int32)
+    sc = np.array([1.0, 2.0, 3.0, -1.0, 0.0, 0.5], np.float32)
+    import rank_adapter_gemm_segmented_amd as ml
+    y = ml.linear(dc.x, dc.W, dc.pool, i32(ss), i32(sa), i32(sr), f32(sc), lora_on=1, workspace=dc.ws)
+    torch.cuda.synchronize()
+    pool = oracle.PackedPool(c.adapters, c.capacity, c.d_in, c.d_out)
+    y_ref = oracle.linear(c.x, c.W, pool, ss, sa, sr, sc, None, 1)
+    compare(y_host(y), y_ref, 2e-2, "empty segments")
+
+
+def test_zero_tokens_is_noop():
+    c = make_custom_case(22, "bf16", 64, 64, [0], {0: 8})
+    dc = DeviceCase(c)
+    import rank_adapter_gemm_segmented_amd as ml
+    x0 = dc.x[:0]
+    y0 = ml.linear(x0, dc.W, dc.pool, dc.seg_start, dc.seg_adapter, dc.seg_rank, dc.seg_scale,
+                   lora_on=1, workspace=dc.ws)
+    torch.cuda.synchronize()
+    assert y0.shape == (0, 64)
+
+
+def test_lora_off_ignores_null_metadata():
+    c = make_case("decode_bf16")
+    dc = _dev("decode_bf16")
+    import rank_adapter_gemm_segmented_amd as ml
+    y = ml.linear(dc.x, dc.W, dc.pool, None, None, None, None, lora_on=0, workspace=dc.ws)
+    torch.cuda.synchronize()
+    y_ref = oracle.linear(c.x, c.W, oracle.PackedPool({}, 1, c.d_in, c.d_out), None, None, None, None,
+                          None, 0, threads=oracle_threads())
+    compare(y_host(y), y_ref, 2e-2, "lora_off null metadata")
