@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Benchmark of the multi-LoRA segmented linear layer on one MI355X.
+
+One step = one call of the whole layer (segment lookup, shrink, base GEMM,
+fused expand, store) over one synthetic batch. The default workload is the
+decode-shaped batch: q_proj 4096->4096, 64 tokens (one per request), 32 rank-16
+adapters assigned uniformly at random and grouped by the caller, bf16 with fp32
+accumulation. Inputs are seeded synthetic data (no real model or adapters).
+
+Timing: W untimed warm-up steps, then K steps back to back on one stream,
+bracketed by synchronizations and HIP events recorded on that stream. Each
+step uses a different buffer set (W, adapter pool, x, y, workspace), rotating
+over >= 1 GiB so the 256 MB Infinity Cache cannot hold the working set: the
+bytes come from HBM.
+
+Reported (one JSON line on stdout):
+  value      effective HBM GB/s of the LoRA-on pass = unique bytes / step time,
+             unique bytes = W + touched adapters' A and B + x + y;
+  tflops     effective TFLOP/s, flops = 2 T d_in d_out + sum_tokens 2 r (d_in + d_out);
+  lora_off   the same shape with lora_on = 0 (the drafter pass), and the
+             LoRA-on overhead t_on / t_off - 1 next to the byte-floor ratio;
+  roofline   the layer kernel against MI355X's 8 TB/s HBM peak, with HBM
+             traffic from rocprofv3 counters when they match the current
+             kernel sources;
+  cpu_baseline  the fp64 oracle on the host cores over the same batch.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("multi-LoRA linear eff. TFLOP/s + HBM GB/s (% roofline); "
+          "LoRA-on vs LoRA-off overhead")
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+CSRC = os.path.join(ROOT, "rank_adapter_gemm_segmented_amd", "csrc")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".h")):
+            with open(os.path.join(CSRC, f), "rb") as fh:
+                h.update(f.encode())
+                h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode_bf16",
+                    choices=["decode_bf16", "verify_bf16", "hetero_bf16", "prefill_bf16", "tiny_f32"])
+    ap.add_argument("--proj", default="q", help="prefill projection")
+    ap.add_argument("--rotate-gib", type=float, default=1.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time (wall x threads) of the oracle baseline")
+    ap.add_argument("--profile", action="store_true",
+                    help="short run for rocprofv3: a few steps plus one 256 MiB calibration copy")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this layer is built and timed on a single MI355X "
+              "(no sharding or collectives); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import rank_adapter_gemm_segmented_amd as ml
+    from gpu_util import f32, i32, to_dev
+    from mlora_inputs import make_case
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    case = make_case(args.workload, args.proj)
+    T, d_in, d_out = case.n_tokens, case.d_in, case.d_out
+    es = 2 if case.dtype == "bf16" else 4
+    touched = case.touched_adapters()
+    lora_bytes = sum((case.adapters[a].rank * d_in + d_out * case.adapters[a].rank) * es for a in touched)
+    base_bytes = (d_out * d_in + T * d_in + T * d_out) * es
+    bytes_on, bytes_off = base_bytes + lora_bytes, base_bytes
+    ranks = np.array([case.adapters[int(a)].rank if a >= 0 else 0 for a in case.token_adapter])
+    flops_off = 2.0 * T * d_in * d_out
+    flops_on = flops_off + float(np.sum(2.0 * ranks * (d_in + d_out)))
+
+    # ---- buffer sets -------------------------------------------------------
+    tdt = torch.bfloat16 if case.dtype == "bf16" else torch.float32
+    W0 = to_dev(case.W, case.dtype)
+    x0 = to_dev(case.x, case.dtype)
+    pool0 = ml.Pool(d_in, d_out, tdt, case.max_rank, case.capacity)
+    for aid in sorted(case.adapters):
+        ad = case.adapters[aid]
+        pool0.register(aid, to_dev(ad.A, case.dtype), to_dev(ad.B, case.dtype))
+    set_bytes = W0.numel() * es + pool0.arena.numel() + x0.numel() * es + T * d_out * es
+    n_sets = 2 if args.profile else max(2, int(np.ceil(args.rotate_gib * (1 << 30) / set_bytes)))
+    sets = []
+    for i in range(n_sets):
+        if i == 0:
+            W, x, pool = W0, x0, pool0
+        else:
+            W, x = W0.clone(), x0.clone()
+            pool = ml.Pool(d_in, d_out, tdt, case.max_rank, case.capacity)
+            pool.arena.copy_(pool0.arena)
+        y = torch.empty((T, d_out), dtype=tdt, device=dev)
+        ws = pool.workspace(T)
+        sets.append((W, x, pool, y, ws))
+    if case.sorted_input:
+        meta = (i32(case.seg_start), i32(case.seg_adapter), i32(case.seg_rank), f32(case.seg_scale))
+    else:
+        tok = i32(case.token_adapter)
+        sc = f32(case.adapter_scale)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+
+    def step(i, lora_on):
+        W, x, pool, y, ws = sets[i % n_sets]
+        if case.sorted_input:
+            ml.linear(x, W, pool, *meta, lora_on=lora_on, out=y, workspace=ws)
+        else:
+            ml.linear_tokens(x, W, pool, tok, sc, lora_on=lora_on, out=y, workspace=ws)
+
+    def timed(lora_on, steps, warmup):
+        for i in range(warmup):
+            step(i, lora_on)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps):
+            step(i, lora_on)
+        e1.record(stream)
+        e1.synchronize()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps   # ms per step
+
+    steps = 5 if args.profile else args.steps
+    warmup = 2 if args.profile else args.warmup
+    ms_on = timed(1, steps, warmup)
+    ms_off = timed(0, steps, warmup)
+    print(f"[bench] {case.name}: lora_on {ms_on * 1e3:.2f} us/step, lora_off {ms_off * 1e3:.2f} us/step, "
+          f"{n_sets} buffer sets of {set_bytes / 2**20:.1f} MiB", file=sys.stderr, flush=True)
+
+    if args.profile:
+        # calibration copy of a known size for the FETCH_SIZE / WRITE_SIZE counters
+        n = 256 << 20
+        src = torch.ones(n // 2, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] calibration copy of {n} bytes done", file=sys.stderr, flush=True)
+        return
+
+    gbs_on = bytes_on / (ms_on * 1e-3) / 1e9
+    gbs_off = bytes_off / (ms_off * 1e-3) / 1e9
+    tf_on = flops_on / (ms_on * 1e-3) / 1e12
+    tf_off = flops_off / (ms_off * 1e-3) / 1e12
+
+    # ---- HBM traffic from committed counter runs (only if sources match) ----
+    traffic = None
+    src_hash = kernel_source_hash()
+    if os.path.exists(TRAFFIC_FILE):
+        try:
+            tr = json.load(open(TRAFFIC_FILE))
+            ent = tr.get(case.name, {})
+            if ent.get("kernel_source_hash") == src_hash:
+                traffic = ent.get("bytes_per_step")
+        except (ValueError, OSError):
+            traffic = None
+
+    roofline = {"bound": "hbm", "achieved": round(gbs_on, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs_on / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "algorithmic_bytes": bytes_on, "kernel_source_hash": src_hash}
+    if case.name.startswith("prefill"):
+        roofline.update({"bound": "mfma", "achieved": round(tf_on, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf_on / MFMA_BF16_PEAK_TFLOPS, 4)})
+
+    # ---- CPU baseline: the fp64 oracle on the host cores -------------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = len(os.sched_getaffinity(0))
+        pool_o = oracle.PackedPool(case.adapters, case.capacity, d_in, d_out)
+        rows = None
+        n_rows = T
+        # bounded sample: whole batch when it is small, else a prefix of rows
+        per_row = 2.0 * d_in * d_out
+        max_rows = max(1, int(4e10 / per_row))
+        if T > max_rows:
+            rows = np.arange(max_rows, dtype=np.int32)
+            n_rows = max_rows
+        reps, t_total = 0, 0.0
+        while t_total * threads < args.cpu_seconds or reps == 0:
+            t0 = time.perf_counter()
+            oracle.case_linear(case, 1, rows=rows, threads=threads, pool=pool_o)
+            t_total += time.perf_counter() - t0
+            reps += 1
+            if reps >= 50:
+                break
+        t_batch = t_total / reps * (T / n_rows)
+        cpu = {"value": round(bytes_on / t_batch / 1e9, 4), "unit": "GB/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"{n_rows} of {T} rows of the {case.name} batch, lora_on=1, fp64, "
+                         f"{reps} repetitions, {t_total:.1f} s wall; value scaled to the whole batch",
+               "seconds_per_batch": round(t_batch, 4)}
+
+    cfg = {"workload": case.name, "tokens": T, "d_in": d_in, "d_out": d_out,
+           "adapters_touched": len(touched), "segments": case.n_seg if case.sorted_input else None,
+           "ranks": sorted(set(case.adapters[a].rank for a in touched)), "lora_on": 1,
+           "buffer_sets": n_sets, "unique_bytes_lora_on": bytes_on, "unique_bytes_lora_off": bytes_off}
+    out = {
+        "metric": METRIC, "value": round(gbs_on, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_on, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": case.dtype,
+        "data": "synthetic (seeded Gaussian weights, adapters and activations)",
+        "config": cfg,
+        "tflops": round(tf_on, 2), "pct_hbm_roofline": round(100 * gbs_on / HBM_PEAK_GBS, 2),
+        "lora_off": {"ms_per_step": round(ms_off, 6), "gbs": round(gbs_off, 1), "tflops": round(tf_off, 2),
+                     "pct_hbm_roofline": round(100 * gbs_off / HBM_PEAK_GBS, 2)},
+        "lora_on_overhead": round(ms_on / ms_off - 1.0, 4),
+        "byte_floor_ratio": round(bytes_on / bytes_off, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

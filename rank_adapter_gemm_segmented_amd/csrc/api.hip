@@ -20,12 +20,14 @@ struct mlora_pool_s {
   long long slot_elems = 0;  // elements per slot (multiple of 128)
   long long b_offset = 0;    // elements from slot start to B
   int32_t* dev_rank = nullptr;
+  void* zeros = nullptr;     // kZeroBytes of zeros, never written after creation
   std::vector<int> host_rank;
 };
 
 namespace {
 
 constexpr size_t kAlign = 256;
+constexpr size_t kZeroBytes = 4096;   // zero block at the end of the pool arena
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -52,7 +54,8 @@ bool shape_ok(int d_in, int d_out, int dtype, int max_rank, int capacity) {
 
 // Workspace layout for up to T tokens.
 struct WsLayout {
-  size_t err, token_index, seg_start, seg_adapter, seg_rank, seg_scale, n_seg, counts, v_part, total;
+  size_t err, token_index, seg_start, seg_adapter, seg_rank, seg_scale, n_seg, counts, v_part,
+      ypart, total;
 };
 
 int r_ws_of(int max_rank) { return (max_rank + 15) / 16 * 16; }
@@ -70,7 +73,13 @@ WsLayout ws_layout(const mlora_pool_s* p, int T) {
   L.seg_scale = take(t1 * 4);
   L.n_seg = take(16);
   L.counts = take(t1 * 4);
-  L.v_part = take((size_t)kMaxShrinkSplit * T * r_ws_of(p->max_rank) * 4);
+  int n_tiles = 0, kc = 0, n_chunks = 0;
+  decode_plan(p->d_in, p->d_out, &n_tiles, &kc, &n_chunks);
+  const int splits = n_chunks > kMaxShrinkSplit ? n_chunks : kMaxShrinkSplit;
+  L.v_part = take((size_t)splits * T * r_ws_of(p->max_rank) * 4);
+  // decode partial tiles, only for token counts the decode path takes
+  const size_t tt = T <= 16 ? 16 : T <= 32 ? 32 : 64;
+  L.ypart = take(p->dtype == MLORA_BF16 && T <= 64 ? (size_t)n_chunks * n_tiles * 64 * tt * 4 : 0);
   L.total = o;
   return L;
 }
@@ -78,6 +87,7 @@ WsLayout ws_layout(const mlora_pool_s* p, int T) {
 PoolView view_of(const mlora_pool_s* p) {
   PoolView v;
   v.base = p->base;
+  v.zeros = p->zeros;
   v.rank = p->dev_rank;
   v.slot_elems = p->slot_elems;
   v.b_offset = p->b_offset;
@@ -87,6 +97,13 @@ PoolView view_of(const mlora_pool_s* p) {
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MLORA_OK : MLORA_ERR_HIP; }
+
+// MLORA_FORCE_PATH=decode|gemm overrides the bf16 path choice (for tests and
+// measurements); unset or anything else chooses by token count.
+int forced_path() {
+  const char* e = getenv("MLORA_FORCE_PATH");
+  return (e && !strcmp(e, "decode")) ? 1 : (e && !strcmp(e, "gemm")) ? 2 : 0;
+}
 
 int check_launch() { return hip_status(hipGetLastError()); }
 
@@ -108,6 +125,26 @@ int run_linear(const void* x, const void* W, mlora_pool_s* pool, const SegView& 
   a.r_ws = r_ws_of(pool->max_rank);
   a.seg_grid = lora_on ? sv.n_seg : 0;
   if (pool->dtype == MLORA_BF16) {
+    const int fp = forced_path();
+    const bool dec_ok = decode_supported(T, lora_on ? sv.n_seg : 0);
+    if (dec_ok && fp != 2) {
+      DecodeArgs d;
+      d.x = x;
+      d.W = W;
+      d.y = y;
+      d.T = T;
+      d.d_in = pool->d_in;
+      d.d_out = pool->d_out;
+      d.lora_on = lora_on;
+      d.sv = sv;
+      d.pv = a.pv;
+      d.ypart = (float*)(ws + L.ypart);
+      d.v_part = a.v_part;
+      d.r_ws = a.r_ws;
+      decode_plan(pool->d_in, pool->d_out, &d.n_tiles, &d.kc, &d.n_chunks);
+      launch_decode_bf16(d, stream);
+      return check_launch();
+    }
     a.ks = choose_shrink_split_bf16(pool->d_in, a.seg_grid);
     launch_linear_bf16(a, stream);
   } else {
@@ -142,7 +179,7 @@ size_t mlora_pool_bytes(int d_in, int d_out, int dtype, int max_rank, int capaci
   long long se, bo;
   slot_geometry(d_in, d_out, max_rank, &se, &bo);
   const size_t slots = align_up((size_t)capacity * (size_t)se * elem_size(dtype), kAlign);
-  return slots + align_up((size_t)capacity * 4, kAlign);
+  return slots + align_up((size_t)capacity * 4, kAlign) + kZeroBytes;
 }
 
 int mlora_pool_create(void* dev_mem, size_t bytes, int d_in, int d_out, int dtype, int max_rank,
@@ -166,8 +203,10 @@ int mlora_pool_create(void* dev_mem, size_t bytes, int d_in, int d_out, int dtyp
   slot_geometry(d_in, d_out, max_rank, &p->slot_elems, &p->b_offset);
   const size_t slots = align_up((size_t)capacity * (size_t)p->slot_elems * p->elem, kAlign);
   p->dev_rank = (int32_t*)((char*)dev_mem + slots);
+  p->zeros = (char*)dev_mem + slots + align_up((size_t)capacity * 4, kAlign);
   p->host_rank.assign(capacity, 0);
   launch_fill_u32(p->dev_rank, (size_t)capacity, 0u, stream);
+  launch_fill_u32(p->zeros, kZeroBytes / 4, 0u, stream);
   const int st = check_launch();
   if (st != MLORA_OK) {
     delete p;

@@ -60,9 +60,12 @@ __device__ __forceinline__ int find_segment(const int32_t* __restrict__ seg_star
 
 __device__ __forceinline__ int round_up8(int r) { return (r + 7) & ~7; }
 
+constexpr int kZeroBlockElems = 2048;   // bf16 elements in the pool's zero block (4 KB)
+
 // Everything a kernel needs to find an adapter in the pool.
 struct PoolView {
   const void* base;        // slot 0
+  const void* zeros;       // 4 KB of zeros (read in place of absent operands)
   const int32_t* rank;     // registered rank per slot (device table)
   long long slot_elems;    // elements per slot
   long long b_offset;      // element offset of B inside a slot (= max_rank * d_in)

@@ -25,6 +25,27 @@ struct LinearArgs {
 };
 
 constexpr int kMaxShrinkSplit = 16;
+constexpr int kMaxRankWs = 256;   // largest v row pitch (max_rank rounded up to 16)
+
+// Small-T (decode) path: split-K streaming kernel + finishing kernel.
+constexpr int kDecMaxKc = 1024;   // largest d_in chunk per item
+constexpr int kDecMaxSeg = 256;   // most segments the decode path handles
+
+struct DecodeArgs {
+  const void* x;
+  const void* W;
+  void* y;
+  int T, d_in, d_out;
+  int lora_on;
+  SegView sv;
+  PoolView pv;
+  float* ypart;    // workspace: partial tiles [n_chunks][n_tiles][4][T/16 blocks][256]
+  float* v_part;   // workspace: shrink partials [n_chunks][T][r_ws]
+  int r_ws;
+  int n_tiles;     // ceil(d_out / 64)
+  int kc;          // d_in chunk width (multiple of 64)
+  int n_chunks;    // ceil(d_in / kc)
+};
 
 // metadata kernels (kernels_meta.hip)
 void launch_token_map(const int32_t* seg_start, const int32_t* seg_adapter, int T, int S,
@@ -43,6 +64,11 @@ void launch_set_slot_rank(int32_t* table, int id, int rank, hipStream_t st);
 // bf16 path (kernels_bf16.hip)
 void launch_linear_bf16(const LinearArgs& a, hipStream_t st);
 int choose_shrink_split_bf16(int d_in, int seg_grid);
+
+// decode path (kernels_decode.hip)
+bool decode_supported(int T, int n_seg_bound);
+void decode_plan(int d_in, int d_out, int* n_tiles, int* kc, int* n_chunks);
+void launch_decode_bf16(const DecodeArgs& a, hipStream_t st);
 
 // fp32 path (kernels_f32.hip)
 void launch_linear_f32(const LinearArgs& a, hipStream_t st);

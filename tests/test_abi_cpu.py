@@ -50,7 +50,7 @@ def _geometry(d_in, d_out, elem, max_rank, capacity):
     b = d_out * ((max_rank + 7) // 8 * 8)
     slot = (b_off + b + 127) // 128 * 128
     slots = (capacity * slot * elem + 255) // 256 * 256
-    return slots + (capacity * 4 + 255) // 256 * 256
+    return slots + (capacity * 4 + 255) // 256 * 256 + 4096
 
 
 @pytest.mark.parametrize("shape", [(4096, 4096, 1, 16, 32), (5120, 5120, 1, 64, 512),

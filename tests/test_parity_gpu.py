@@ -161,3 +161,27 @@ def test_lora_off_ignores_null_metadata():
     y_ref = oracle.linear(c.x, c.W, oracle.PackedPool({}, 1, c.d_in, c.d_out), None, None, None, None,
                           None, 0, threads=oracle_threads())
     compare(y_host(y), y_ref, 2e-2, "lora_off null metadata")
+
+
+# ---------------------------------------------------------------------------
+# both bf16 paths (split-K decode path and tiled GEMM path) on the same shapes
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("path", ["decode", "gemm"])
+@pytest.mark.parametrize("idx", range(5))
+def test_forced_paths(path, idx, monkeypatch):
+    shapes = [
+        (81, 4096, 4096, sorted(np.random.default_rng(81).integers(0, 32, size=64).tolist()), 16),
+        (82, 1024, 520, sorted(np.random.default_rng(82).integers(-1, 6, size=40).tolist()), 32),
+        (83, 2056, 64, [0] * 9 + [1] * 7, 64),
+        (84, 8192, 300, sorted(np.random.default_rng(84).integers(0, 64, size=33).tolist()), 8),
+        (85, 640, 4096, [3], 16),
+    ]
+    seed, d_in, d_out, ids, r = shapes[idx]
+    monkeypatch.setenv("MLORA_FORCE_PATH", path)
+    log(f"[parity] forced {path}: {d_in}->{d_out} T={len(ids)} r={r}")
+    ranks = {a: r for a in set(ids) if a >= 0}
+    c = make_custom_case(seed, "bf16", d_in, d_out, ids, ranks)
+    dc = DeviceCase(c)
+    check_case(dc, 1, what=f"forced {path} lora_on=1")
+    check_case(dc, 0, what=f"forced {path} lora_on=0")
