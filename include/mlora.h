@@ -69,6 +69,7 @@ typedef enum {
 #define MLORA_MAX_RANK 256
 #define MLORA_MAX_TOKENS (1 << 20)
 #define MLORA_MAX_UNSORTED_TOKENS 8192
+#define MLORA_MAX_SEGMENTS 16384
 
 /* Human-readable text for a status code (static storage). */
 const char* mlora_status_string(int status);
@@ -144,8 +145,10 @@ int mlora_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t st
  *                          token_index[p] of x and y (NULL = identity, i.e. the
  *                          caller already grouped its rows).
  * lora_on: 0 (LoRA-off drafter pass: y = W x) or 1.
- * Errors: MLORA_ERR_INVALID_ARG, MLORA_ERR_SHAPE, MLORA_ERR_WORKSPACE (host
- * checks). Inconsistent metadata is not detected here (see mlora_validate). */
+ * n_seg: 1 .. MLORA_MAX_SEGMENTS when lora_on = 1.
+ * Errors: MLORA_ERR_INVALID_ARG, MLORA_ERR_SHAPE, MLORA_ERR_WORKSPACE,
+ * MLORA_ERR_METADATA (n_seg < 1) from host checks. Inconsistent device
+ * metadata is not detected here (see mlora_validate). */
 int mlora_linear(const void* x, const void* W, mlora_pool_t pool, const int32_t* seg_start,
                  const int32_t* seg_adapter, const int32_t* seg_rank, const float* seg_scale,
                  const int32_t* token_index, int n_tokens, int n_seg, int lora_on, void* y,

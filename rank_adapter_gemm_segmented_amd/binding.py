@@ -36,7 +36,7 @@ class MloraError(RuntimeError):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is not built: run `python -m rank_adapter_gemm_segmented_amd.build` "
+            f"{LIB_PATH} is not built: run `python rank_adapter_gemm_segmented_amd/build.py` "
             "(or __graft_entry__.build()) first. There is no fallback path.")
     lib = ctypes.CDLL(LIB_PATH)
     P, I, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t

@@ -1,6 +1,6 @@
 """Compile the gfx950 HIP library ``libmlora.so`` in-tree with hipcc.
 
-Usage: ``python -m rank_adapter_gemm_segmented_amd.build`` (or
+Usage: ``python rank_adapter_gemm_segmented_amd/build.py`` (or
 ``__graft_entry__.build()``). Objects go to ``_build/`` next to this file.
 """
 from __future__ import annotations
@@ -17,7 +17,7 @@ LIB = os.path.join(HERE, "libmlora.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.hip", "kernels_meta.hip", "kernels_bf16.hip", "kernels_decode.hip", "kernels_f32.hip"]
+SOURCES = ["api.hip", "kernels_meta.hip", "kernels_gemm.hip", "kernels_decode.hip", "kernels_f32.hip"]
 
 # Packed fp32 VALU ops are disabled for every device compile.
 FLAGS = [

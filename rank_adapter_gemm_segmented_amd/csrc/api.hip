@@ -55,7 +55,7 @@ bool shape_ok(int d_in, int d_out, int dtype, int max_rank, int capacity) {
 // Workspace layout for up to T tokens.
 struct WsLayout {
   size_t err, token_index, seg_start, seg_adapter, seg_rank, seg_scale, n_seg, counts, v_part,
-      ypart, total;
+      ypart, pos_info, v_fin, total;
 };
 
 int r_ws_of(int max_rank) { return (max_rank + 15) / 16 * 16; }
@@ -80,6 +80,8 @@ WsLayout ws_layout(const mlora_pool_s* p, int T) {
   // decode partial tiles, only for token counts the decode path takes
   const size_t tt = T <= 16 ? 16 : T <= 32 ? 32 : 64;
   L.ypart = take(p->dtype == MLORA_BF16 && T <= 64 ? (size_t)n_chunks * n_tiles * 64 * tt * 4 : 0);
+  L.pos_info = take((size_t)T * 16);
+  L.v_fin = take((size_t)T * r_ws_of(p->max_rank) * 4);
   L.total = o;
   return L;
 }
@@ -122,6 +124,8 @@ int run_linear(const void* x, const void* W, mlora_pool_s* pool, const SegView& 
   a.sv = sv;
   a.pv = view_of(pool);
   a.v_part = (float*)(ws + L.v_part);
+  a.pos_info = (int4*)(ws + L.pos_info);
+  a.v_fin = (float*)(ws + L.v_fin);
   a.r_ws = r_ws_of(pool->max_rank);
   a.seg_grid = lora_on ? sv.n_seg : 0;
   if (pool->dtype == MLORA_BF16) {
@@ -145,7 +149,7 @@ int run_linear(const void* x, const void* W, mlora_pool_s* pool, const SegView& 
       launch_decode_bf16(d, stream);
       return check_launch();
     }
-    a.ks = choose_shrink_split_bf16(pool->d_in, a.seg_grid);
+    a.ks = choose_shrink_split_bf16(pool->d_in, shrink_items_bound(T, a.seg_grid));
     launch_linear_bf16(a, stream);
   } else {
     a.ks = 1;
@@ -289,7 +293,8 @@ int mlora_linear(const void* x, const void* W, mlora_pool_t pool, const int32_t*
   SegView sv{};
   if (lora_on) {
     if (!seg_start || !seg_adapter || !seg_rank || !seg_scale) return MLORA_ERR_INVALID_ARG;
-    if (n_seg < 1 || n_seg > n_tokens + pool->capacity + 1) return MLORA_ERR_METADATA;
+    if (n_seg < 1) return MLORA_ERR_METADATA;
+    if (n_seg > MLORA_MAX_SEGMENTS) return MLORA_ERR_SHAPE;
     sv.seg_start = seg_start;
     sv.seg_adapter = seg_adapter;
     sv.seg_rank = seg_rank;

@@ -1,0 +1,603 @@
+// kernels_gemm.hip -- bf16 multi-LoRA linear for larger token counts on gfx950.
+//
+// y_i = W x_i + scale_s * B_a (A_a x_i) ("Multi-LoRA Serving in Practice",
+// section "Core Principle", displayed formula), per adapter segment
+// ("InvisibleLoRA" abstract). Two launches:
+//
+//  k_shrink2  v = A_a x per segment, fp32, split over d_in chunks into
+//             deterministic partials; also writes a per-position table
+//             {segment, adapter, rank, scale} read by the GEMM epilogue.
+//  k_gemm2    W x as a tiled GEMM on v_mfma_f32_32x32x16_bf16: block tile of
+//             BR W rows x BT sorted positions over the whole of d_in, both
+//             operands staged through LDS (double-buffered, 144-byte row pitch
+//             so 16-lane operand reads are conflict-free). The epilogue adds
+//             scale * B_a v on the same accumulators with MFMAs (v split into
+//             a bf16 high and low part, ~16 mantissa bits) and stores y once.
+//
+// MFMA 32x32x16 bf16 layout: lane l supplies row l%32 and k-slots 8*(l/32)..+7
+// of each operand; result register v of lane l is row 8*(v/4)+4*(l/32)+v%4,
+// column l%32. The A operand is W (rows = output features) and the B operand
+// is x (columns = tokens), so each lane ends with runs of 4 consecutive
+// features of one token: 8-byte stores of y.
+#include "common.h"
+#include "launch.h"
+
+namespace mlora {
+
+__device__ __forceinline__ f32x4_t mfma16g(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16_t mfma32g(u32x4_t a, u32x4_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Shrink. grid (items, d_in chunks), 4 waves. An item is one 64-position block
+// of one segment (segments longer than 64 positions give several items, so
+// long prefill segments spread over many workgroups). Each workgroup finds its
+// item with a scan of the segment starts in LDS. Chunk c covers k-steps
+// [c*nks/ks, (c+1)*nks/ks) of 32, walked in groups of 16 k-steps (512 d_in):
+// wave w takes k-steps w, w+4, w+8, w+12 of each group and accumulates in
+// registers; the four waves are summed in a fixed order through LDS.
+// MFMA rows = sorted positions (16 per block), columns = rank index j.
+// ---------------------------------------------------------------------------
+constexpr int kShrKs = 4;         // k-steps per wave per group
+constexpr int kShrMaxSeg = MLORA_MAX_SEGMENTS;  // segments the item scan handles
+
+__global__ __launch_bounds__(256) void k_shrink2(LinearArgs a) {
+  const int item = blockIdx.x, c = blockIdx.y;
+  const SegView& sv = a.sv;
+  const int S = min(seg_count(sv), kShrMaxSeg);
+  const int T = a.T, d_in = a.d_in;
+  const int tid = threadIdx.x;
+  extern __shared__ int sst[];   // [S + 1] segment starts (dynamic LDS)
+  __shared__ int part[256];
+  __shared__ int found[2];
+  __shared__ float red[4][kWave][17];
+
+  // ---- which (segment, block) is this item? --------------------------------
+  for (int i = tid; i <= S; i += 256) sst[i] = sv.seg_start[i];
+  __syncthreads();
+  const int per = (S + 255) / 256;
+  int cnt = 0;
+  for (int i = tid * per; i < min(S, tid * per + per); ++i) {
+    const int len = min(sst[i + 1], T) - max(sst[i], 0);
+    cnt += len > 0 ? (len + 63) / 64 : 0;
+  }
+  part[tid] = cnt;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  if (tid == 0) found[0] = -1;
+  __syncthreads();
+  {
+    const int lo = part[tid] - cnt;   // items before this thread's segments
+    if (item >= lo && item < part[tid]) {
+      int acc = lo;
+      for (int i = tid * per; i < min(S, tid * per + per); ++i) {
+        const int len = min(sst[i + 1], T) - max(sst[i], 0);
+        const int nb = len > 0 ? (len + 63) / 64 : 0;
+        if (item < acc + nb) {
+          found[0] = i;
+          found[1] = item - acc;
+          break;
+        }
+        acc += nb;
+      }
+    }
+  }
+  __syncthreads();
+  const int s = found[0];
+  if (s < 0) return;   // uniform: past the last item
+  const int ps = max(sst[s], 0) + 64 * found[1];
+  const int pe = min(min(sst[s + 1], T), ps + 64);
+  int r;
+  const int ad = seg_adapter_checked(sv, a.pv, s, &r);
+  if (c == 0) {   // per-position table for the GEMM epilogue
+    const float scl = ad >= 0 ? sv.seg_scale[s] : 0.f;
+    for (int p = ps + tid; p < pe; p += 256) {
+      int4 e;
+      e.x = s;
+      e.y = ad;
+      e.z = ad >= 0 ? r : 0;
+      e.w = __float_as_int(scl);
+      a.pos_info[p] = e;
+    }
+  }
+  if (ad < 0) return;
+
+  const uint16_t* __restrict__ x = (const uint16_t*)a.x;
+  const uint16_t* __restrict__ Aa = (const uint16_t*)a.pv.base + (long long)ad * a.pv.slot_elems;
+  const int nks = (d_in + 31) / 32;
+  const int kb = (int)((long long)c * nks / a.ks);
+  const int ke = (int)((long long)(c + 1) * nks / a.ks);
+  const int wave = tid / kWave, lane = tid % kWave;
+  const int l16 = lane % 16, kq = 8 * (lane / 16);
+
+  // x rows of the block's positions (fixed over k)
+  const uint16_t* xrow[4];
+  bool pval[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    const int p = ps + rb * 16 + l16;
+    pval[rb] = p < pe;
+    int row = sv.token_index ? sv.token_index[pval[rb] ? p : ps] : (pval[rb] ? p : ps);
+    row = min(max(row, 0), T - 1);
+    xrow[rb] = x + (long long)row * d_in;
+  }
+
+  for (int jg = 0; jg < r; jg += 64) {
+    f32x4_t acc[4][4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int kg = kb; kg < ke; kg += 4 * kShrKs) {
+      int koff[kShrKs];
+      bool kval[kShrKs];
+#pragma unroll
+      for (int i = 0; i < kShrKs; ++i) {
+        const int ks = kg + wave + 4 * i;
+        kval[i] = ks < ke && ks * 32 + kq < d_in;
+        koff[i] = kval[i] ? ks * 32 + kq : 0;
+      }
+      u32x4_t af[4][kShrKs], xf[4][kShrKs];
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const int j = jg + cb * 16 + l16;
+        const bool jv = j < r;
+        const uint16_t* arow = Aa + (long long)(jv ? j : 0) * d_in;
+#pragma unroll
+        for (int i = 0; i < kShrKs; ++i) {
+          const u32x4_t v = ld16(arow + koff[i]);
+          af[cb][i] = (jv && kval[i]) ? v : zero_u32x4();
+        }
+      }
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int i = 0; i < kShrKs; ++i) {
+          const u32x4_t v = ld16(xrow[rb] + koff[i]);
+          xf[rb][i] = (pval[rb] && kval[i]) ? v : zero_u32x4();
+        }
+#pragma unroll
+      for (int i = 0; i < kShrKs; ++i)
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = mfma16g(xf[rb][i], af[cb][i], acc[rb][cb]);
+    }
+    // fixed-order sum of the four waves, one 16-position block at a time
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      if (ps + rb * 16 >= pe) break;   // uniform
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) red[wave][lane][cb * 4 + v] = acc[rb][cb][v];
+      __syncthreads();
+      for (int e = tid; e < kWave * 16; e += 256) {
+        const int l = e / 16, q = e % 16, cb = q / 4, v = q % 4;
+        const int p = ps + rb * 16 + 4 * (l / 16) + v;
+        const int j = jg + cb * 16 + (l % 16);
+        const float sum = ((red[0][l][q] + red[1][l][q]) + red[2][l][q]) + red[3][l][q];
+        if (p < pe && j < r) a.v_part[((long long)c * T + p) * a.r_ws + j] = sum;
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Finalize: v_fin[p][j] = scale_p * sum_c v_part[c][p][j] (chunk order) for
+// j < rank_p, else 0. One thread per 4 rank columns of one position.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_vfinal(LinearArgs a) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  const int q4 = a.r_ws / 4;
+  if (e >= a.T * q4) return;
+  const int p = e / q4, j = 4 * (e % q4);
+  const int4 pi = a.pos_info[p];
+  const int rk = (pi.y >= 0 && pi.y < a.pv.capacity) ? min(pi.z, a.pv.max_rank) : 0;
+  f32x4_t sum = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  if (j < rk) {
+    f32x4_t part[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      part[c] = *(const f32x4_t*)(a.v_part + ((long long)min(c, a.ks - 1) * a.T + p) * a.r_ws + j);
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      if (c < a.ks) {
+        sum[0] += part[c][0];
+        sum[1] += part[c][1];
+        sum[2] += part[c][2];
+        sum[3] += part[c][3];
+      }
+    const float sc = __int_as_float(pi.w);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sum[i] = (j + i < rk) ? sum[i] * sc : 0.f;
+  }
+  *(f32x4_t*)(a.v_fin + (long long)p * a.r_ws + j) = sum;
+}
+
+// ---------------------------------------------------------------------------
+// GEMM + fused expand
+// ---------------------------------------------------------------------------
+constexpr int kGKB = 64;            // k per pipeline stage
+constexpr int kBatch = 8;           // independent loads per thread in bulk LDS copies
+constexpr int kGPitch = kGKB + 8;   // LDS row pitch in bf16 (144 bytes)
+
+template <int BR, int BT, int WR, int WT, int PD>
+struct GCfg {
+  static constexpr int NWR = BR / WR, NWT = BT / WT;
+  static constexpr int NW = NWR * NWT;
+  static constexpr int NT = NW * kWave;
+  static constexpr int MR = WR / 32, MT = WT / 32;        // 32x32 blocks per wave
+  static constexpr int ROWS = BR + BT;                     // LDS rows per stage
+  static constexpr int CPT = ROWS * (kGKB / 8) / NT;       // 16-byte pieces per thread per stage
+  static constexpr int STAGE = ROWS * kGPitch;             // bf16 per stage
+  static constexpr int MAIN_BYTES = 2 * STAGE * 2;
+  // small row tiles get extra LDS so the epilogue stages many segment runs at once
+  static constexpr int LDS_BYTES = MAIN_BYTES > 96 * 1024 ? MAIN_BYTES : 96 * 1024;
+  static_assert((ROWS * (kGKB / 8)) % NT == 0, "stage pieces must divide the threads");
+};
+
+template <int BR, int BT, int WR, int WT, int PD>
+__global__ __launch_bounds__((BR / WR) * (BT / WT) * kWave) void k_gemm2(LinearArgs a) {
+  using C = GCfg<BR, BT, WR, WT, PD>;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_BYTES / 2];
+  __shared__ int4 pinfo[BT];
+
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int l32 = lane % 32, kh = 8 * (lane / 32);
+  const int T = a.T, d_in = a.d_in, d_out = a.d_out;
+  const int n_rt = (d_out + BR - 1) / BR;
+  const int rt = blockIdx.x % n_rt, tt = blockIdx.x / n_rt;
+  const int r0 = rt * BR, t0 = tt * BT;
+  const int wr = wave / C::NWT, wt = wave % C::NWT;
+  const uint16_t* __restrict__ x = (const uint16_t*)a.x;
+  const uint16_t* __restrict__ W = (const uint16_t*)a.W;
+  const uint16_t* zeros = (const uint16_t*)a.pv.zeros;
+
+  // loader: piece q = tid + NT*i -> stage row R = q / 8 (W rows first, then
+  // positions), 16-byte column q % 8
+  const uint16_t* src[C::CPT];
+  int dst[C::CPT];
+#pragma unroll
+  for (int i = 0; i < C::CPT; ++i) {
+    const int q = tid + C::NT * i;
+    const int R = q / 8, cc = q % 8;
+    dst[i] = R * kGPitch + cc * 8;
+    if (R < BR) {
+      src[i] = W + (long long)min(r0 + R, d_out - 1) * d_in + cc * 8;
+    } else {
+      const int p = min(t0 + R - BR, T - 1);
+      int row = a.sv.token_index ? a.sv.token_index[p] : p;
+      row = min(max(row, 0), T - 1);
+      src[i] = x + (long long)row * d_in + cc * 8;
+    }
+  }
+  f32x16_t acc[C::MR][C::MT];
+#pragma unroll
+  for (int m = 0; m < C::MR; ++m)
+#pragma unroll
+    for (int n = 0; n < C::MT; ++n)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[m][n][v] = 0.f;
+
+  // PD stages of global loads in flight in a register ring; LDS is double-buffered
+  u32x4_t stg[PD][C::CPT];
+  auto load = [&](int st, u32x4_t* dstr) {
+    const int k0 = st * kGKB;
+#pragma unroll
+    for (int i = 0; i < C::CPT; ++i) {
+      const int k = k0 + (tid + C::NT * i) % 8 * 8;
+      // past d_in: read the zero block (address select keeps the load branch-free)
+      dstr[i] = ld16(k < d_in ? src[i] + k0 : zeros);
+    }
+  };
+  auto store = [&](int buf, const u32x4_t* srcr) {
+#pragma unroll
+    for (int i = 0; i < C::CPT; ++i) *(u32x4_t*)&lds[buf * C::STAGE + dst[i]] = srcr[i];
+  };
+  auto compute = [&](int buf) {
+    const uint16_t* Ls = lds + buf * C::STAGE;
+#pragma unroll
+    for (int kk = 0; kk < kGKB / 16; ++kk) {
+      u32x4_t af[C::MR], bf[C::MT];
+#pragma unroll
+      for (int m = 0; m < C::MR; ++m)
+        af[m] = *(const u32x4_t*)&Ls[(wr * WR + m * 32 + l32) * kGPitch + kk * 16 + kh];
+#pragma unroll
+      for (int n = 0; n < C::MT; ++n)
+        bf[n] = *(const u32x4_t*)&Ls[(BR + wt * WT + n * 32 + l32) * kGPitch + kk * 16 + kh];
+#pragma unroll
+      for (int m = 0; m < C::MR; ++m)
+#pragma unroll
+        for (int n = 0; n < C::MT; ++n) acc[m][n] = mfma32g(af[m], bf[n], acc[m][n]);
+    }
+  };
+
+  // Stage count padded to a multiple of PD: stages past d_in read the zero
+  // block and add nothing. Every load and store inside the loop is
+  // unconditional, so the compiler's vmcnt waits stay exact (a conditional load
+  // would make them drain the whole prefetch ring at each merge point).
+  const int nst = (d_in + kGKB - 1) / kGKB;
+  const int nst_pad = (nst + PD - 1) / PD * PD;
+  // stage k lives in ring slot k % PD
+  load(0, stg[0]);
+  store(0, stg[0]);
+#pragma unroll
+  for (int k = 1; k <= PD; ++k) load(k, stg[k % PD]);
+  __syncthreads();
+  for (int st0 = 0; st0 < nst_pad - PD; st0 += PD) {
+#pragma unroll
+    for (int u = 0; u < PD; ++u) {
+      const int st = st0 + u;
+      compute(st & 1);
+      store((st + 1) & 1, stg[(u + 1) % PD]);
+      load(st + 1 + PD, stg[(u + 1) % PD]);
+      __syncthreads();
+    }
+  }
+  {  // last PD stages: nothing further to prefetch
+    const int st0 = nst_pad - PD;
+#pragma unroll
+    for (int u = 0; u < PD; ++u) {
+      const int st = st0 + u;
+      compute(st & 1);
+      if (u + 1 < PD) store((st + 1) & 1, stg[(u + 1) % PD]);
+      __syncthreads();
+    }
+  }
+
+  // ---- expand: acc += B_a (scale v) per segment run, on MFMA ---------------
+  // Runs of one segment among the tile's positions are listed once, with each
+  // position's run index. Per rank chunk of up to 64 columns, scale*v of the
+  // tile's positions is staged in LDS already split into a bf16 high and low
+  // part; B slices (BR rows) of a group of runs are staged next to it, the
+  // next group's slices loading into registers while the current group's
+  // MFMAs run. A token block only visits the runs that overlap it.
+  if (a.lora_on) {
+    constexpr int MAXP = 16;                         // B pieces per thread per group
+    const int RC = a.r_ws < 64 ? a.r_ws : 64;        // rank columns per chunk (16, 32 or 64)
+    const int VP = RC + 8;                           // hi/lo row pitch (bf16)
+    const int BP = RC + 8;                           // bs row pitch (bf16)
+    const int VS_BYTES = 2 * BT * VP * 2;
+    int G = (C::LDS_BYTES - VS_BYTES) / (BR * BP * 2);
+    G = min(G, MAXP * C::NT / (BR * (RC / 8)));      // runs per group (>= 1)
+    uint16_t* vsh = lds;
+    uint16_t* vsl = lds + BT * VP;
+    uint16_t* bs = lds + VS_BYTES / 2;
+    __shared__ int rstart[BT + 1];
+    __shared__ int prun[BT];
+    __shared__ int rflag[C::NT];
+    __shared__ int nrun;
+
+    const int teff = min(BT, T - t0);
+    for (int t = tid; t < BT; t += C::NT) {
+      const int p = t0 + t;
+      int4 e = make_int4(-1, -1, 0, 0);
+      if (p < T) {
+        e = a.pos_info[p];
+        // clamp whatever the table holds (only meaningful for valid metadata)
+        if (e.y < 0 || e.y >= a.pv.capacity || e.z <= 0) { e.y = -1; e.z = 0; }
+        e.z = min(e.z, a.pv.max_rank);
+      }
+      pinfo[t] = e;
+    }
+    __syncthreads();
+    {  // run list: thread t owns positions [t*PPT, t*PPT + PPT)
+      constexpr int PPT = (BT + C::NT - 1) / C::NT;
+      int cnt = 0;
+      for (int i = 0; i < PPT; ++i) {
+        const int t = tid * PPT + i;
+        if (t < teff && (t == 0 || pinfo[t].x != pinfo[t - 1].x)) ++cnt;
+      }
+      rflag[tid] = cnt;
+      __syncthreads();
+      for (int off = 1; off < C::NT; off <<= 1) {
+        const int v = tid >= off ? rflag[tid - off] : 0;
+        __syncthreads();
+        rflag[tid] += v;
+        __syncthreads();
+      }
+      int idx = rflag[tid] - cnt;
+      for (int i = 0; i < PPT; ++i) {
+        const int t = tid * PPT + i;
+        if (t < teff) {
+          if (t == 0 || pinfo[t].x != pinfo[t - 1].x) rstart[idx++] = t;
+          prun[t] = idx - 1;
+        }
+      }
+      if (tid == C::NT - 1) {
+        nrun = rflag[C::NT - 1];
+        rstart[rflag[C::NT - 1]] = teff;
+      }
+      __syncthreads();
+    }
+    const int nr = nrun;
+
+    // B pieces of group g0: run g0+g, row, 16-byte column q
+    u32x4_t bq[MAXP];
+    // rc: columns of the current chunk (a multiple of 16, at most RC)
+    auto load_b = [&](int jc0, int rc, int g0) {
+      const int ppr = BR * (rc / 8);                 // pieces per run
+      const int nbs = min(G, nr - g0) * ppr;
+#pragma unroll
+      for (int u = 0; u < MAXP; ++u) {
+        const int e = min(tid + u * C::NT, max(nbs - 1, 0));
+        const int g = e / ppr, rem = e % ppr;
+        const int row = rem / (rc / 8), q = rem % (rc / 8);
+        const int4 pi = pinfo[rstart[min(g0 + g, nr - 1)]];
+        const int j = jc0 + 8 * q;
+        const bool ok = nbs > 0 && pi.y >= 0 && j < pi.z;
+        // an absent slice reads the zero block (no select on the loaded value)
+        const uint16_t* src = ok ? (const uint16_t*)a.pv.base + (long long)pi.y * a.pv.slot_elems +
+                                       a.pv.b_offset + (long long)min(r0 + row, d_out - 1) * round_up8(pi.z) + j
+                                 : zeros;
+        bq[u] = ld16(src);
+      }
+    };
+    auto store_b = [&](int rc, int g0) {
+      const int ppr = BR * (rc / 8);
+      const int nbs = min(G, nr - g0) * ppr;
+#pragma unroll
+      for (int u = 0; u < MAXP; ++u) {
+        const int e = tid + u * C::NT;
+        if (e < nbs) {
+          const int g = e / ppr, rem = e % ppr;
+          *(u32x4_t*)&bs[(g * BR + rem / (rc / 8)) * BP + 8 * (rem % (rc / 8))] = bq[u];
+        }
+      }
+    };
+
+    for (int jc0 = 0; jc0 < a.r_ws; jc0 += RC) {
+      const int rc = min(RC, a.r_ws - jc0);
+      if (nr > 0) load_b(jc0, rc, 0);
+      // scale * v of the tile's positions, split into bf16 high and low parts
+      const int nvs = BT * (rc / 4);
+      for (int e0 = tid; e0 < nvs; e0 += C::NT * kBatch) {
+        f32x4_t v[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int e = min(e0 + u * C::NT, nvs - 1);
+          const int t = e / (rc / 4), q = e % (rc / 4);
+          const int tt = t < teff ? t : 0;
+          v[u] = *(const f32x4_t*)(a.v_fin + (long long)(t0 + tt) * a.r_ws + jc0 + 4 * q);
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int e = e0 + u * C::NT;
+          if (e < nvs) {
+            const int t = e / (rc / 4), q = e % (rc / 4);
+            uint32_t h[2], l[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+              const float v0 = t < teff ? v[u][2 * i] : 0.f, v1 = t < teff ? v[u][2 * i + 1] : 0.f;
+              const uint16_t h0 = f32_to_bf16_bits(v0), h1 = f32_to_bf16_bits(v1);
+              h[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+              l[i] = (uint32_t)f32_to_bf16_bits(v0 - bf16_bits_to_f32(h0)) |
+                     ((uint32_t)f32_to_bf16_bits(v1 - bf16_bits_to_f32(h1)) << 16);
+            }
+            *(u32x2_t*)&vsh[t * VP + 4 * q] = u32x2_t{h[0], h[1]};
+            *(u32x2_t*)&vsl[t * VP + 4 * q] = u32x2_t{l[0], l[1]};
+          }
+        }
+      }
+      for (int g0 = 0; g0 < nr; g0 += G) {
+        store_b(rc, g0);
+        __syncthreads();
+        if (g0 + G < nr) load_b(jc0, rc, g0 + G);   // lands while the MFMAs below run
+        const int gend = min(g0 + G, nr) - 1;
+#pragma unroll
+        for (int n = 0; n < C::MT; ++n) {
+          const int tb0 = wt * WT + n * 32;
+          if (tb0 >= teff) continue;                            // uniform
+          const int glo = max(prun[tb0], g0);
+          const int ghi = min(prun[min(tb0 + 31, teff - 1)], gend);
+          const int tl = tb0 + l32;
+          for (int g = glo; g <= ghi; ++g) {                    // uniform
+            const int rs = rstart[g], re = rstart[g + 1];
+            const int4 pi = pinfo[rs];
+            if (pi.y < 0) continue;
+            const bool in = tl >= rs && tl < re;
+            for (int jc = 0; jc < rc && jc0 + jc < pi.z; jc += 16) {
+              u32x4_t hiu = *(const u32x4_t*)&vsh[min(tl, BT - 1) * VP + jc + kh];
+              u32x4_t lou = *(const u32x4_t*)&vsl[min(tl, BT - 1) * VP + jc + kh];
+              if (!in) { hiu = zero_u32x4(); lou = zero_u32x4(); }
+#pragma unroll
+              for (int m = 0; m < C::MR; ++m) {
+                const u32x4_t bop = *(const u32x4_t*)&bs[((g - g0) * BR + wr * WR + m * 32 + l32) * BP + jc + kh];
+                acc[m][n] = mfma32g(bop, hiu, acc[m][n]);
+                acc[m][n] = mfma32g(bop, lou, acc[m][n]);
+              }
+            }
+          }
+        }
+        __syncthreads();
+      }
+    }
+  }
+
+  // ---- store y (bf16, RNE), rows scattered through token_index ------------
+  uint16_t* __restrict__ y = (uint16_t*)a.y;
+#pragma unroll
+  for (int n = 0; n < C::MT; ++n) {
+    const int p = t0 + wt * WT + n * 32 + l32;
+    if (p >= T) continue;
+    int row = a.sv.token_index ? a.sv.token_index[p] : p;
+    row = min(max(row, 0), T - 1);
+    uint16_t* yr = y + (long long)row * d_out;
+#pragma unroll
+    for (int m = 0; m < C::MR; ++m) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int nb = r0 + wr * WR + m * 32 + 8 * q + 4 * (lane / 32);
+        float av[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) av[v] = acc[m][n][4 * q + v];
+        if (nb + 3 < d_out && (d_out & 3) == 0) {
+          u32x2_t pk;
+          pk.x = (uint32_t)f32_to_bf16_bits(av[0]) | ((uint32_t)f32_to_bf16_bits(av[1]) << 16);
+          pk.y = (uint32_t)f32_to_bf16_bits(av[2]) | ((uint32_t)f32_to_bf16_bits(av[3]) << 16);
+          *(u32x2_t*)(yr + nb) = pk;
+        } else {
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (nb + v < d_out) yr[nb + v] = f32_to_bf16_bits(av[v]);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+// d_in chunks of the shrink: enough workgroups for the GPU, at most 8 (the
+// GEMM epilogue sums the partials), each chunk at least one 512-wide group.
+int choose_shrink_split_bf16(int d_in, int items) {
+  const int groups = (d_in + 511) / 512;
+  int ks = 1;
+  while (ks < 8 && ks * 2 <= groups && items * ks < 512) ks *= 2;
+  return ks;
+}
+
+int shrink_items_bound(int T, int n_seg_bound) {
+  return (n_seg_bound < kShrMaxSeg ? n_seg_bound : kShrMaxSeg) + (T + 63) / 64;
+}
+
+template <int BR, int BT, int WR, int WT, int PD>
+static void launch_g(const LinearArgs& a, hipStream_t st) {
+  const int n_rt = (a.d_out + BR - 1) / BR, n_tt = (a.T + BT - 1) / BT;
+  hipLaunchKernelGGL((k_gemm2<BR, BT, WR, WT, PD>), dim3(n_rt * n_tt),
+                     dim3(GCfg<BR, BT, WR, WT, PD>::NT), 0, st, a);
+}
+
+// Tile choice: large batches take 256x256 tiles (MFMA-bound, ~30 B/clk of L2
+// per CU); otherwise a tile spans every position of the batch (one read of x
+// per CU) with as few W rows as keep the CUs busy.
+void launch_linear_bf16(const LinearArgs& a, hipStream_t st) {
+  if (a.lora_on && a.seg_grid > 0) {
+    const int nseg = a.seg_grid < kShrMaxSeg ? a.seg_grid : kShrMaxSeg;
+    hipLaunchKernelGGL(k_shrink2, dim3(shrink_items_bound(a.T, a.seg_grid), a.ks), dim3(256),
+                       (size_t)(nseg + 1) * sizeof(int), st, a);
+    const int n4 = a.T * (a.r_ws / 4);
+    hipLaunchKernelGGL(k_vfinal, dim3((n4 + 255) / 256), dim3(256), 0, st, a);
+  }
+  auto tiles = [&](int br, int bt) {
+    return (long long)((a.d_out + br - 1) / br) * ((a.T + bt - 1) / bt);
+  };
+  constexpr long long kFill = 192;   // tiles that keep most of the 256 CUs busy
+  if (a.T > 128 && tiles(256, 256) >= kFill) launch_g<256, 256, 128, 128, 1>(a, st);
+  else if (a.T > 128 && tiles(128, 256) >= kFill) launch_g<128, 256, 64, 128, 2>(a, st);
+  else if (a.T > 128 && tiles(64, 256) >= kFill) launch_g<64, 256, 64, 64, 3>(a, st);
+  else launch_g<64, 128, 32, 64, 4>(a, st);
+}
+
+}  // namespace mlora

@@ -19,6 +19,8 @@ struct LinearArgs {
   SegView sv;
   PoolView pv;
   float* v_part;   // workspace: shrink partials [ks][T][r_ws] fp32
+  int4* pos_info;  // workspace: per sorted position {segment, adapter, rank, scale bits}
+  float* v_fin;    // workspace: scale * v per sorted position [T][r_ws] fp32
   int r_ws;        // row pitch of v_part (max_rank rounded up to 16)
   int ks;          // number of d_in chunks of the shrink (1..kMaxShrinkSplit)
   int seg_grid;    // number of segments to cover (upper bound)
@@ -61,9 +63,10 @@ void launch_validate(const int32_t* seg_start, const int32_t* seg_adapter, const
 void launch_fill_u32(void* p, size_t n_words, uint32_t v, hipStream_t st);
 void launch_set_slot_rank(int32_t* table, int id, int rank, hipStream_t st);
 
-// bf16 path (kernels_bf16.hip)
+// bf16 path for larger token counts (kernels_gemm.hip)
 void launch_linear_bf16(const LinearArgs& a, hipStream_t st);
 int choose_shrink_split_bf16(int d_in, int seg_grid);
+int shrink_items_bound(int T, int n_seg_bound);
 
 // decode path (kernels_decode.hip)
 bool decode_supported(int T, int n_seg_bound);

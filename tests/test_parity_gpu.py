@@ -167,20 +167,26 @@ def test_lora_off_ignores_null_metadata():
 # both bf16 paths (split-K decode path and tiled GEMM path) on the same shapes
 # ---------------------------------------------------------------------------
 
+_FORCED_SHAPES = [
+    # (seed, d_in, d_out, sorted ids, rank or {id: rank})
+    (81, 4096, 4096, sorted(np.random.default_rng(81).integers(0, 32, size=64).tolist()), 16),
+    (82, 1024, 520, sorted(np.random.default_rng(82).integers(-1, 6, size=40).tolist()), 32),
+    (83, 2056, 64, [0] * 9 + [1] * 7, 64),
+    (84, 8192, 300, sorted(np.random.default_rng(84).integers(0, 64, size=33).tolist()), 8),
+    (85, 640, 4096, [3], 16),
+    # rank chunks wider than 64 columns: max rank 80 (a 64 + 16 split) and 256
+    (86, 512, 200, [0] * 30 + [1] * 20 + [2] * 14, {0: 80, 1: 40, 2: 72}),
+    (87, 256, 136, [-1] * 3 + [0] * 25 + [1] * 36 + [2] * 3, {0: 256, 1: 100, 2: 1}),
+]
+
+
 @pytest.mark.parametrize("path", ["decode", "gemm"])
-@pytest.mark.parametrize("idx", range(5))
+@pytest.mark.parametrize("idx", range(len(_FORCED_SHAPES)))
 def test_forced_paths(path, idx, monkeypatch):
-    shapes = [
-        (81, 4096, 4096, sorted(np.random.default_rng(81).integers(0, 32, size=64).tolist()), 16),
-        (82, 1024, 520, sorted(np.random.default_rng(82).integers(-1, 6, size=40).tolist()), 32),
-        (83, 2056, 64, [0] * 9 + [1] * 7, 64),
-        (84, 8192, 300, sorted(np.random.default_rng(84).integers(0, 64, size=33).tolist()), 8),
-        (85, 640, 4096, [3], 16),
-    ]
-    seed, d_in, d_out, ids, r = shapes[idx]
+    seed, d_in, d_out, ids, r = _FORCED_SHAPES[idx]
     monkeypatch.setenv("MLORA_FORCE_PATH", path)
     log(f"[parity] forced {path}: {d_in}->{d_out} T={len(ids)} r={r}")
-    ranks = {a: r for a in set(ids) if a >= 0}
+    ranks = r if isinstance(r, dict) else {a: r for a in set(ids) if a >= 0}
     c = make_custom_case(seed, "bf16", d_in, d_out, ids, ranks)
     dc = DeviceCase(c)
     check_case(dc, 1, what=f"forced {path} lora_on=1")
