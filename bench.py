@@ -68,7 +68,70 @@ def parse():
                     help="target CPU time (wall x threads) of the oracle baseline")
     ap.add_argument("--profile", action="store_true",
                     help="short run for rocprofv3: a few steps plus one 256 MiB calibration copy")
+    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="host only: turn the counter_collection.csv files of two --profile runs "
+                         "(--pmc FETCH_SIZE, --pmc WRITE_SIZE) into the workload's entry of "
+                         "profiles/traffic.json")
     return ap.parse_args()
+
+
+CALIB_BYTES = 256 << 20
+
+
+def ingest_counters(workload: str, kernels, fetch_csv: str, write_csv: str) -> dict:
+    """HBM traffic per layer call from two rocprofv3 --pmc runs of --profile.
+
+    Each counter is scaled by what it reads for the calibration copy of
+    CALIB_BYTES (the largest __amd_rocclr_copyBuffer dispatch: it reads and
+    writes CALIB_BYTES). The layer's kernels are averaged over their LoRA-on
+    dispatches and summed."""
+    import csv
+
+    def per_kernel(path):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    out = {"kernel_source_hash": kernel_source_hash(), "calibration_bytes": CALIB_BYTES}
+    total = 0.0
+    for key, path in (("fetch", fetch_csv), ("write", write_csv)):
+        vals = per_kernel(path)
+        calib = max(vals.get("__amd_rocclr_copyBuffer", [0.0]))
+        if calib <= 0:
+            raise SystemExit(f"{path}: no calibration copy found")
+        factor = CALIB_BYTES / (calib * 1024.0)
+        kib = {}
+        for k in kernels:
+            hits = [v for n, v in vals.items() if f"mlora::{k}" in n or n.startswith(f"void mlora::{k}<")]
+            if not hits:
+                raise SystemExit(f"{path}: kernel {k} not found")
+            flat = [x for h in hits for x in h]
+            kib[k] = sum(flat) / len(flat)
+        out[f"{key}_kib_per_dispatch"] = {k: round(v, 1) for k, v in kib.items()}
+        out[f"{key}_scale"] = round(factor, 4)
+        total += sum(kib.values()) * 1024.0 * factor
+    out["bytes_per_step"] = int(round(total))
+    allt = {}
+    if os.path.exists(TRAFFIC_FILE):
+        allt = json.load(open(TRAFFIC_FILE))
+    allt[workload] = out
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(allt, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    return out
+
+
+def layer_kernels(case):
+    """Kernels of one LoRA-on layer call, run back to back on one stream: the
+    split-K stream + finish pair for T <= 64 in bf16; segment build (unsorted
+    input), shrink, v fold and the tiled GEMM with fused expand above that;
+    shrink + GEMM for fp32."""
+    if case.dtype == "bf16" and case.n_tokens <= 64:
+        return ["k_stream_bf16", "k_finish_bf16"]
+    if case.dtype == "bf16":
+        return (["k_build_segments"] if not case.sorted_input else []) + ["k_shrink2", "k_vfinal", "k_gemm2"]
+    return ["k_shrink_f32", "k_gemm_f32"]
 
 
 def main():
@@ -86,9 +149,13 @@ def main():
     from gpu_util import f32, i32, to_dev
     from mlora_inputs import make_case
 
+    case = make_case(args.workload, args.proj)
+    if args.ingest_counters:
+        ent = ingest_counters(case.name, layer_kernels(case), *args.ingest_counters)
+        print(json.dumps({case.name: ent}))
+        return
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
-    case = make_case(args.workload, args.proj)
     T, d_in, d_out = case.n_tokens, case.d_in, case.d_out
     es = 2 if case.dtype == "bf16" else 4
     touched = case.touched_adapters()
@@ -150,14 +217,10 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps   # ms per step
 
-    steps = 5 if args.profile else args.steps
-    warmup = 2 if args.profile else args.warmup
-    ms_on = timed(1, steps, warmup)
-    ms_off = timed(0, steps, warmup)
-    print(f"[bench] {case.name}: lora_on {ms_on * 1e3:.2f} us/step, lora_off {ms_off * 1e3:.2f} us/step, "
-          f"{n_sets} buffer sets of {set_bytes / 2**20:.1f} MiB", file=sys.stderr, flush=True)
-
     if args.profile:
+        # counter runs: LoRA-on calls only, then a copy of known size
+        timed(1, 5, 2)
+        print(f"[bench] {case.name}: 7 lora_on calls done", file=sys.stderr, flush=True)
         # calibration copy of a known size for the FETCH_SIZE / WRITE_SIZE counters
         n = 256 << 20
         src = torch.ones(n // 2, dtype=torch.bfloat16, device=dev)
@@ -166,6 +229,11 @@ def main():
         torch.cuda.synchronize()
         print(f"[bench] calibration copy of {n} bytes done", file=sys.stderr, flush=True)
         return
+
+    ms_on = timed(1, args.steps, args.warmup)
+    ms_off = timed(0, args.steps, args.warmup)
+    print(f"[bench] {case.name}: lora_on {ms_on * 1e3:.2f} us/step, lora_off {ms_off * 1e3:.2f} us/step, "
+          f"{n_sets} buffer sets of {set_bytes / 2**20:.1f} MiB", file=sys.stderr, flush=True)
 
     gbs_on = bytes_on / (ms_on * 1e-3) / 1e9
     gbs_off = bytes_off / (ms_off * 1e-3) / 1e9
@@ -184,9 +252,11 @@ def main():
         except (ValueError, OSError):
             traffic = None
 
+    kernels = layer_kernels(case)
     roofline = {"bound": "hbm", "achieved": round(gbs_on, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gbs_on / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "algorithmic_bytes": bytes_on, "kernel_source_hash": src_hash}
+                "algorithmic_bytes": bytes_on, "us_per_call": round(ms_on * 1e3, 3),
+                "kernels": kernels, "kernel_source_hash": src_hash}
     if case.name.startswith("prefill"):
         roofline.update({"bound": "mfma", "achieved": round(tf_on, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf_on / MFMA_BF16_PEAK_TFLOPS, 4)})
@@ -196,6 +266,9 @@ def main():
     if not args.no_cpu_baseline:
         import oracle
         threads = len(os.sched_getaffinity(0))
+        if os.environ.get("OMP_NUM_THREADS", "").isdigit():
+            threads = min(threads, int(os.environ["OMP_NUM_THREADS"]))
+        threads = max(1, min(threads, 16))
         pool_o = oracle.PackedPool(case.adapters, case.capacity, d_in, d_out)
         rows = None
         n_rows = T
