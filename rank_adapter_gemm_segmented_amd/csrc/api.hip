@@ -75,7 +75,8 @@ WsLayout ws_layout(const mlora_pool_s* p, int T) {
   L.counts = take(t1 * 4);
   int n_tiles = 0, kc = 0, n_chunks = 0;
   decode_plan(p->d_in, p->d_out, &n_tiles, &kc, &n_chunks);
-  const int splits = n_chunks > kMaxShrinkSplit ? n_chunks : kMaxShrinkSplit;
+  // shrink partial slices: split-K of the large-T path, or 8 waves per d_in chunk at T <= 64
+  const int splits = n_chunks * 8 > kMaxShrinkSplit ? n_chunks * 8 : kMaxShrinkSplit;
   L.v_part = take((size_t)splits * T * r_ws_of(p->max_rank) * 4);
   // decode partial tiles, only for token counts the decode path takes
   const size_t tt = T <= 16 ? 16 : T <= 32 ? 32 : 64;
@@ -144,6 +145,7 @@ int run_linear(const void* x, const void* W, mlora_pool_s* pool, const SegView& 
       d.pv = a.pv;
       d.ypart = (float*)(ws + L.ypart);
       d.v_part = a.v_part;
+      d.pos = a.pos_info;
       d.r_ws = a.r_ws;
       decode_plan(pool->d_in, pool->d_out, &d.n_tiles, &d.kc, &d.n_chunks);
       launch_decode_bf16(d, stream);

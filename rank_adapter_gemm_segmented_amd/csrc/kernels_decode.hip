@@ -32,22 +32,23 @@ __device__ __forceinline__ f32x4_t mfma16d(u32x4_t a, u32x4_t b, f32x4_t c) {
 }
 
 constexpr int kDecThreads = 512;                   // 8 waves
+constexpr int kDecWaves = kDecThreads / kWave;
 constexpr int kDecRows = 64;                       // W rows per item (4 blocks of 16)
 constexpr int kDecXPitch = kDecMaxKc + 8;          // LDS row pitch of the x chunk (bf16)
 constexpr int kDecWSteps = kDecMaxKc / 2 / 32;     // 32-wide k-steps per wave (16)
+constexpr int kDecWPre = 8;                        // W k-steps requested before the MFMA loop
+constexpr int kDecRowWin = 32;                     // shrink rows per item found by table lookup
 constexpr int kDecASteps = kDecMaxKc / 8 / 32;     // shrink k-steps per wave per row block (4)
 
 template <int TT>
 struct DecSmem {
   uint16_t xs[TT * kDecXPitch];
-  union {
-    float red[4][kWave][4 * (TT / 16)];            // second-half partials of the W rows
-    float vred[8][kWave][4];                       // shrink partials per wave
-  } u;
+  float red[4][kWave][4 * (TT / 16)];              // second-half partials of the W rows
   int pref[kDecMaxSeg + 1];                        // shrink-row prefix over segments
   int sad[kDecMaxSeg];                             // adapter of each segment (-1: none)
   int sps[kDecMaxSeg], spe[kDecMaxSeg];            // token range of each segment
-  int rseg[16], rj[16];                            // current shrink row block: segment, rank row
+  int rseg[kDecRowWin], rj[kDecRowWin];            // item's first shrink rows: segment, rank row
+  int posseg[64];                                  // segment of each sorted position (-1: none)
 };
 
 // Partial tile layout (fragment-major): for chunk c, n-tile i, row block rb,
@@ -129,25 +130,6 @@ __global__ __launch_bounds__(kDecThreads) void k_stream_bf16(DecodeArgs a) {
     xr[i] = sel(t < T && xcol_ok, ld16(x + (long long)xrow[i] * d_in + xk));
   }
 
-  // ---- 2. W rows -> MFMA A-operand registers, every k-step at once ---------
-  // wave w: row block rb = w % 4, k-half kh = w / 4 of the chunk
-  const int rb = wave & 3, kh = wave >> 2;
-  const int nrow = tile * kDecRows + rb * 16 + l16;
-  const bool row_ok = nrow < d_out;
-  const int half_steps = (nks + 1) / 2;
-  const int ks_begin = kh ? half_steps : 0;
-  const int ks_end = kh ? nks : half_steps;
-  u32x4_t wr[kDecWSteps];
-  {
-    const uint16_t* wrow = W + (long long)(row_ok ? nrow : d_out - 1) * d_in + k0;
-#pragma unroll
-    for (int s = 0; s < kDecWSteps; ++s) {
-      const int k = (ks_begin + s) * 32 + kq;
-      const bool ok = row_ok && (ks_begin + s) < ks_end && k < kc;
-      wr[s] = sel(ok, ld_nt16(wrow + (k < kc ? k : kc - 8)));
-    }
-  }
-
   // ---- 3. segment table and shrink-row prefix (one wave, no block barrier) -
   if (lora && wave == kMetaWave) {
     // lane owns segments 4*lane .. 4*lane+3; rows to shrink per segment are its
@@ -175,13 +157,32 @@ __global__ __launch_bounds__(kDecThreads) void k_stream_bf16(DecodeArgs a) {
       if (lane >= off) inc += up;
     }
     int run = inc - tot;
+    int p0[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int sg = lane * 4 + i;
+      p0[i] = run;
       if (sg < nseg) sm.pref[sg] = run;
       run += rr[i];
     }
     if (lane == kWave - 1) sm.pref[nseg] = inc;   // total rows (nseg <= 256 = 4 * 64)
+    // Direct lookup tables by scatter, so no lane needs a search later: the
+    // segment and rank row of the item's first kDecRowWin shrink rows, and the
+    // segment of every sorted position (item 0 writes the position table).
+    const int rtot = __shfl(inc, kWave - 1, kWave);
+    const int qb0 = (int)((long long)tile * rtot / a.n_tiles);
+    const int qe0 = min((int)((long long)(tile + 1) * rtot / a.n_tiles), qb0 + kDecRowWin);
+    if (lane < T) sm.posseg[lane] = -1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int sg = lane * 4 + i;
+      for (int q = max(p0[i], qb0); q < min(p0[i] + rr[i], qe0); ++q) {
+        sm.rseg[q - qb0] = sg;
+        sm.rj[q - qb0] = q - p0[i];
+      }
+      if (sg < nseg)
+        for (int q = max(m_st[i], 0); q < min(m_st[i + 1], T); ++q) sm.posseg[q] = sg;
+    }
   }
 
   // ---- 5. x registers -> LDS -----------------------------------------------
@@ -191,6 +192,46 @@ __global__ __launch_bounds__(kDecThreads) void k_stream_bf16(DecodeArgs a) {
     *(u32x4_t*)&sm.xs[t * XP + xcol * 8] = xr[i];
   }
   __syncthreads();
+
+  // ---- 2. W rows -> MFMA A-operand registers --------------------------------
+  // wave w: row block rb = w % 4, k-half kh = w / 4 of the chunk. The first
+  // kDecWPre k-steps are requested now; the MFMA loop requests one more step
+  // per step it consumes, so the MFMAs run while W streams in instead of
+  // after the wave has finished issuing the whole chunk. W is requested only
+  // once x is in LDS: x's misses would otherwise queue behind the W stream of
+  // every CU. Addresses past the chunk or d_out are clamped into the row:
+  // their products meet zero x columns or land in discarded rows; steps that
+  // belong to the other k-half read zeros. No select on a loaded value.
+  const int rb = wave & 3, kh = wave >> 2;
+  const int nrow = tile * kDecRows + rb * 16 + l16;
+  const int half_steps = (nks + 1) / 2;
+  const int ks_begin = kh ? half_steps : 0;
+  const int ks_end = kh ? nks : half_steps;
+  const uint16_t* wrow = W + (long long)min(nrow, d_out - 1) * d_in + k0;
+  u32x4_t wr[kDecWSteps];
+  auto load_w = [&](int s) {
+    // steps of the other k-half read the pool's zero block (address select)
+    const int k = (ks_begin + s) * 32 + kq;
+    wr[s] = ld_nt16(ks_begin + s < ks_end ? wrow + min(k, kc - 8) : (const uint16_t*)a.pv.zeros + kq);
+  };
+#pragma unroll
+  for (int s = 0; s < kDecWPre; ++s) load_w(s);
+
+  // ---- per-position table for k_finish ------------------------------------
+  // One item resolves every sorted position's segment once (adapter checked
+  // against the pool's slot table, rank, scale), so the finish kernel reads
+  // one entry per token instead of walking the metadata. Its loads are issued
+  // here and only waited for after the W MFMAs.
+  const bool pos_writer = lora && blockIdx.x == 0 && tid < T;
+  int pos_ad = -1, pos_r = 0, pos_s = 0;
+  float pos_sc = 0.f;
+  if (pos_writer) {
+    const int sg = sm.posseg[tid];
+    pos_s = sg >= 0 ? sg : 0;
+    pos_ad = sg >= 0 ? sm.sad[sg] : -1;
+    pos_r = a.pv.rank[pos_ad >= 0 ? pos_ad : 0];   // registered rank; used after the MFMAs
+    pos_sc = a.sv.seg_scale[pos_s];
+  }
 
   // ---- 4. shrink rows of this item: first two blocks of A rows -------------
   // (after the barrier: the segment table is in LDS; these loads overlap the
@@ -205,9 +246,17 @@ __global__ __launch_bounds__(kDecThreads) void k_stream_bf16(DecodeArgs a) {
     // clamped in-row address whose product meets zero x in LDS
     const int q = qb + l16;
     const bool qok = q < q_end;
-    const int s = seg_of_row(sm.pref, nseg, qok ? q : q_begin);
-    const int ad = sm.sad[s];
-    const int j = (qok ? q : q_begin) - sm.pref[s];
+    const int qq = qok ? q : q_begin;
+    int s, j;
+    if (qb + 16 <= q_begin + kDecRowWin) {   // uniform: rows in the lookup window
+      // (the entry is unset when the item has no rows: qok is false then)
+      s = qok ? min(max(sm.rseg[qq - q_begin], 0), kDecMaxSeg - 1) : 0;
+      j = sm.rj[qq - q_begin];
+    } else {
+      s = seg_of_row(sm.pref, nseg, qq);
+      j = qq - sm.pref[s];
+    }
+    const int ad = qok ? sm.sad[s] : -1;
     const bool rok = qok && nseg > 0 && ad >= 0;
     const uint16_t* arow = rok ? (const uint16_t*)a.pv.base + (long long)ad * a.pv.slot_elems +
                                      (long long)j * d_in + k0
@@ -224,25 +273,71 @@ __global__ __launch_bounds__(kDecThreads) void k_stream_bf16(DecodeArgs a) {
   load_a(q_begin, ar[0]);
   load_a(q_begin + 16, ar[1]);
 
+  // output rows of shrink block qb held by this lane (qb + 4*(lane/16) + v):
+  // segment, rank row, token range, and the token blocks the block covers.
+  // Computed for the first block here, while the W loads are in flight.
+  struct RowInfo { int os[4], oj[4], o0[4], o1[4], tb_lo, tb_hi; };
+  auto row_info = [&](int qb) {
+    RowInfo ri;
+    int tlo = T, thi = 0;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int q = qb + 4 * (lane / 16) + v;
+      ri.os[v] = -1;
+      ri.oj[v] = 0;
+      ri.o0[v] = 0;
+      ri.o1[v] = 0;
+      if (q < q_end) {
+        int sg, jj;
+        if (qb + 16 <= q_begin + kDecRowWin) {   // uniform: rows in the lookup window
+          sg = sm.rseg[q - q_begin];
+          jj = sm.rj[q - q_begin];
+        } else {
+          sg = seg_of_row(sm.pref, nseg, q);
+          jj = q - sm.pref[sg];
+        }
+        ri.os[v] = sg;
+        ri.oj[v] = jj;
+        ri.o0[v] = sm.sps[sg];
+        ri.o1[v] = sm.spe[sg];
+        tlo = min(tlo, ri.o0[v]);
+        thi = max(thi, ri.o1[v]);
+      }
+    }
+    // wave-uniform range: lanes 0, 16, 32 and 48 hold the block's 16 rows
+    tlo = min(tlo, __shfl_xor(tlo, 16, kWave));
+    tlo = min(tlo, __shfl_xor(tlo, 32, kWave));
+    thi = max(thi, __shfl_xor(thi, 16, kWave));
+    thi = max(thi, __shfl_xor(thi, 32, kWave));
+    ri.tb_lo = tlo / 16;
+    ri.tb_hi = thi > tlo ? (thi - 1) / 16 : ri.tb_lo - 1;
+    return ri;
+  };
+  RowInfo ri0 = row_info(q_begin);
+
   // ---- 6. base MFMAs --------------------------------------------------------
   f32x4_t acc[NTB];
 #pragma unroll
   for (int tb = 0; tb < NTB; ++tb) acc[tb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < kDecWSteps; ++s) {
-    const int ks = min(ks_begin + s, kDecMaxKc / 32 - 1);   // zero operands past ks_end
+    if (s + kDecWPre < kDecWSteps) load_w(s + kDecWPre);
+    // x columns past ks_end (past the chunk) are zero in LDS; k-steps past
+    // the LDS chunk are clamped onto such columns
+    const int ks = min(ks_begin + s, kDecMaxKc / 32 - 1);
 #pragma unroll
     for (int tb = 0; tb < NTB; ++tb) {
       const u32x4_t xo = *(const u32x4_t*)&sm.xs[(tb * 16 + l16) * XP + ks * 32 + kq];
       acc[tb] = mfma16d(wr[s], xo, acc[tb]);
     }
+    __builtin_amdgcn_sched_barrier(0);   // keep each step's load next to its MFMAs
   }
   // fixed-order sum of the two k-halves, then one coalesced fragment store
   if (kh == 1) {
 #pragma unroll
     for (int tb = 0; tb < NTB; ++tb)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) sm.u.red[rb][lane][tb * 4 + v] = acc[tb][v];
+      for (int v = 0; v < 4; ++v) sm.red[rb][lane][tb * 4 + v] = acc[tb][v];
   }
   __syncthreads();
   if (kh == 0) {
@@ -250,26 +345,25 @@ __global__ __launch_bounds__(kDecThreads) void k_stream_bf16(DecodeArgs a) {
     for (int tb = 0; tb < NTB; ++tb) {
       f32x4_t o;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) o[v] = acc[tb][v] + sm.u.red[rb][lane][tb * 4 + v];
+      for (int v = 0; v < 4; ++v) o[v] = acc[tb][v] + sm.red[rb][lane][tb * 4 + v];
       *(f32x4_t*)(a.ypart + part_off(c, tile, rb, tb, a.n_tiles, NTB) + lane * 4) = o;
     }
   }
+  if (pos_writer) {
+    const int r = pos_ad >= 0 ? min(sm.pref[pos_s + 1] - sm.pref[pos_s], pos_r) : 0;
+    const int ad = r > 0 ? pos_ad : -1;
+    a.pos[tid] = make_int4(ad, ad >= 0 ? r : 0, __float_as_int(ad >= 0 ? pos_sc : 0.f), 0);
+  }
   if (q_begin >= q_end) return;   // uniform: no shrink rows in this item
-  __syncthreads();                // red is reused as vred below
 
   // ---- 7. shrink row blocks -------------------------------------------------
+  // Each wave writes its own k-slice of the block straight to
+  // v_part[c][wave][t][j] (k_finish sums the 8 * n_chunks slices in a fixed
+  // order): no barrier after the W MFMAs.
   int buf = 0;
   for (int qb = q_begin; qb < q_end; qb += 16, buf ^= 1) {
-    if (tid < 16) {   // row table of this block
-      const int q = qb + tid;
-      int s = -1, j = 0;
-      if (q < q_end) {
-        s = seg_of_row(sm.pref, nseg, q);
-        j = q - sm.pref[s];
-      }
-      sm.rseg[tid] = s;
-      sm.rj[tid] = j;
-    }
+    const RowInfo ri = qb == q_begin ? ri0 : row_info(qb);
+    const int tb_lo = ri.tb_lo, tb_hi = ri.tb_hi;
     f32x4_t vacc[NTB];
 #pragma unroll
     for (int tb = 0; tb < NTB; ++tb) vacc[tb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -278,141 +372,166 @@ __global__ __launch_bounds__(kDecThreads) void k_stream_bf16(DecodeArgs a) {
       const int ks = wave + 8 * st;   // always < 32; operands past the chunk are zero
 #pragma unroll
       for (int tb = 0; tb < NTB; ++tb) {
+        if (tb < tb_lo || tb > tb_hi) continue;
         const u32x4_t xo = *(const u32x4_t*)&sm.xs[(tb * 16 + l16) * XP + ks * 32 + kq];
         vacc[tb] = mfma16d(ar[buf][st], xo, vacc[tb]);
       }
     }
     if (qb + 32 < q_end) load_a(qb + 32, ar[buf]);   // refill this buffer two blocks ahead
-    // reduce the 8 waves in a fixed order, one token block at a time
+    float* vp = a.v_part + ((long long)c * kDecWaves + wave) * T * a.r_ws;
 #pragma unroll
     for (int tb = 0; tb < NTB; ++tb) {
+      if (tb < tb_lo || tb > tb_hi) continue;
+      const int t = tb * 16 + l16;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) sm.u.vred[wave][lane][v] = vacc[tb][v];
-      __syncthreads();
-      if (tid < 256) {
-        const int l = tid / 4, v = tid % 4;
-        const int rr = 4 * (l / 16) + v;      // result row in the block = shrink row qb + rr
-        const int t = tb * 16 + (l % 16);     // result column = sorted token position
-        float sum = 0.f;
-#pragma unroll
-        for (int w = 0; w < 8; ++w) sum += sm.u.vred[w][l][v];
-        const int s = sm.rseg[rr];
-        if (s >= 0 && t >= sm.sps[s] && t < sm.spe[s])
-          a.v_part[((long long)c * T + t) * a.r_ws + sm.rj[rr]] = sum;
-      }
-      __syncthreads();
+      for (int v = 0; v < 4; ++v)
+        if (ri.os[v] >= 0 && t >= ri.o0[v] && t < ri.o1[v]) vp[(long long)t * a.r_ws + ri.oj[v]] = vacc[tb][v];
     }
   }
 }
 
 // ---------------------------------------------------------------------------
 // finish: one workgroup per (n-tile, 16-token block); wave w = row block w.
+// Every load that does not depend on the adapter id is issued first (chunk
+// partials, v partials, the position table, token_index); the B rows follow
+// once the lane's adapter is known.
 // ---------------------------------------------------------------------------
 constexpr int kFinUnroll = 8;
 
 template <int TT>
 __global__ __launch_bounds__(256) void k_finish_bf16(DecodeArgs a) {
   constexpr int NTB = TT / 16;
+  constexpr int kPre = 2;                // B column groups of 8 prefetched (ranks <= 16)
   const int tile = blockIdx.x / NTB, tb = blockIdx.x % NTB;
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid % kWave;
   const int T = a.T, d_out = a.d_out;
   const int rb = wave;
+  const bool lora = a.lora_on != 0;
   __shared__ float vs[16][kMaxRankWs + 4];
-  __shared__ int tseg[16], trank[16];
-  __shared__ int sst[kDecMaxSeg + 1];
+  __shared__ f32x4_t vgrp[4][256];
 
-  // segment starts -> LDS (issued before the partial loads)
-  const int S = a.lora_on ? min(seg_count(a.sv), kDecMaxSeg) : 0;
-  for (int i = tid; i <= S && S > 0; i += 256) sst[i] = a.sv.seg_start[i];
+  const int t = tb * 16 + (lane % 16);   // this lane's token (sorted position)
+  const int tc = min(t, T - 1);
+  const int n = tile * kDecRows + rb * 16 + 4 * (lane / 16);
+  int row = a.sv.token_index ? a.sv.token_index[tc] : tc;
+  const int4 pe = lora ? a.pos[tc] : make_int4(-1, 0, 0, 0);
 
-  // the chunk partials, all loads in flight, summed in chunk order
+  // the chunk partials, all loads in flight
   const float* pbase = a.ypart + part_off(0, tile, rb, tb, a.n_tiles, NTB) + lane * 4;
   const long long cstride = (long long)a.n_tiles * 4 * NTB * 256;
+  f32x4_t p[kFinUnroll];
+#pragma unroll
+  for (int u = 0; u < kFinUnroll; ++u) p[u] = *(const f32x4_t*)(pbase + min(u, a.n_chunks - 1) * cstride);
+
+  // B rows of the lane's adapter (first 16 rank columns), as soon as the
+  // position entry is in
+  const int ad = pe.x, r = min(pe.y, a.pv.max_rank);
+  const bool live = lora && ad >= 0 && ad < a.pv.capacity && r > 0 && t < T;
+  const uint16_t* Bb = (const uint16_t*)(live ? a.pv.base : a.pv.zeros) +
+                       (live ? (long long)ad * a.pv.slot_elems + a.pv.b_offset : 0);
+  const int bld = live ? round_up8(r) : 0;
+  u32x4_t b8[kPre][4];
+#pragma unroll
+  for (int g = 0; g < kPre; ++g)
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      b8[g][v] = ld16(Bb + (live ? (long long)min(n + v, d_out - 1) * bld + min(8 * g, bld - 8) : 0));
+
+  // chunk partials summed in chunk order
   f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int c0 = 0; c0 < a.n_chunks; c0 += kFinUnroll) {
-    f32x4_t p[kFinUnroll];
 #pragma unroll
-    for (int u = 0; u < kFinUnroll; ++u) {
-      const int cc = min(c0 + u, a.n_chunks - 1);
-      p[u] = *(const f32x4_t*)(pbase + cc * cstride);
+  for (int u = 0; u < kFinUnroll; ++u)
+    if (u < a.n_chunks) {
+      acc[0] += p[u][0];
+      acc[1] += p[u][1];
+      acc[2] += p[u][2];
+      acc[3] += p[u][3];
     }
+  for (int c0 = kFinUnroll; c0 < a.n_chunks; c0 += kFinUnroll) {
 #pragma unroll
-    for (int u = 0; u < kFinUnroll; ++u) {
+    for (int u = 0; u < kFinUnroll; ++u) p[u] = *(const f32x4_t*)(pbase + min(c0 + u, a.n_chunks - 1) * cstride);
+#pragma unroll
+    for (int u = 0; u < kFinUnroll; ++u)
       if (c0 + u < a.n_chunks) {
         acc[0] += p[u][0];
         acc[1] += p[u][1];
         acc[2] += p[u][2];
         acc[3] += p[u][3];
       }
-    }
   }
 
-  const int t = tb * 16 + (lane % 16);   // this lane's token (sorted position)
-  const int n = tile * kDecRows + rb * 16 + 4 * (lane / 16);
-  if (S > 0) {
-    __syncthreads();
-    if (tid < 16) {
-      const int tt = tb * 16 + tid;
-      int sg = -1, rk = 0;
-      if (tt < T) {
-        const int s = find_segment(sst, S, tt);
-        if (sst[s] <= tt && tt < sst[s + 1]) {
-          int r;
-          if (seg_adapter_checked(a.sv, a.pv, s, &r) >= 0) { sg = s; rk = r; }
-        }
-      }
-      tseg[tid] = sg;
-      trank[tid] = rk;
-    }
-    __syncthreads();
-    // stage scale * sum_c v_c for the 16 tokens
-    for (int e = tid; e < 16 * a.r_ws; e += 256) {
-      const int ti = e / a.r_ws, jj = e % a.r_ws;
-      const int tt = tb * 16 + ti;
-      const bool live = tseg[ti] >= 0 && jj < trank[ti];
-      const float* vp = a.v_part + (long long)min(tt, T - 1) * a.r_ws + jj;
-      const long long vstride = (long long)T * a.r_ws;
-      float sum = 0.f;
-      for (int c0 = 0; c0 < a.n_chunks; c0 += kFinUnroll) {
-        float q[kFinUnroll];
+  if (lora) {
+    // v of the 16 tokens: sum of the stream kernel's slices [c][w]. A 16-byte
+    // quad of one token is element e; G groups of threads each sum every G-th
+    // slice of an element, then the groups are added in group order.
+    const int nq = a.r_ws / 4;
+    const int E = 16 * nq;
+    const int G = E >= 256 ? 1 : E >= 128 ? 2 : 4;
+    const int nsl = a.n_chunks * kDecWaves;
+    const long long vstride = (long long)T * a.r_ws;
+    for (int e0 = 0; e0 < E; e0 += 256 / G) {
+      const int g = tid % G, e = e0 + tid / G;
+      const int ti = min(e, E - 1) / nq, jq = min(e, E - 1) % nq;
+      const float* vp = a.v_part + (long long)min(tb * 16 + ti, T - 1) * a.r_ws + 4 * jq;
+      f32x4_t sum = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int s0 = g; s0 < nsl; s0 += G * kFinUnroll) {
+        f32x4_t q[kFinUnroll];
 #pragma unroll
-        for (int u = 0; u < kFinUnroll; ++u) q[u] = vp[min(c0 + u, a.n_chunks - 1) * vstride];
+        for (int u = 0; u < kFinUnroll; ++u) q[u] = *(const f32x4_t*)(vp + min(s0 + u * G, nsl - 1) * vstride);
 #pragma unroll
         for (int u = 0; u < kFinUnroll; ++u)
-          if (c0 + u < a.n_chunks) sum += q[u];
+          if (s0 + u * G < nsl) {
+            sum[0] += q[u][0];
+            sum[1] += q[u][1];
+            sum[2] += q[u][2];
+            sum[3] += q[u][3];
+          }
       }
-      vs[ti][jj] = live ? sum * a.sv.seg_scale[tseg[ti]] : 0.f;
+      vgrp[g][tid / G] = sum;
+      __syncthreads();
+      if (tid < 256 / G && e0 + tid < E) {
+        f32x4_t tot = vgrp[0][tid];
+        for (int gg = 1; gg < G; ++gg) {
+          tot[0] += vgrp[gg][tid][0];
+          tot[1] += vgrp[gg][tid][1];
+          tot[2] += vgrp[gg][tid][2];
+          tot[3] += vgrp[gg][tid][3];
+        }
+        const int ee = e0 + tid;
+        *(f32x4_t*)&vs[ee / nq][4 * (ee % nq)] = tot;
+      }
+      __syncthreads();
     }
-    __syncthreads();
-    const int sg = tseg[lane % 16];
-    if (sg >= 0 && t < T) {
-      const int r = trank[lane % 16];
-      const int ad = a.sv.seg_adapter[sg];
-      const int bld = round_up8(r);
-      const uint16_t* Bb = (const uint16_t*)a.pv.base + (long long)ad * a.pv.slot_elems + a.pv.b_offset;
+    if (live) {
       const float* vv = vs[lane % 16];
       float lsum[4] = {0.f, 0.f, 0.f, 0.f};
       for (int j0 = 0; j0 < r; j0 += 8) {
-        u32x4_t b8[4];
+        u32x4_t bq[4];
+        if (j0 < 8 * kPre) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) b8[v] = ld16(Bb + (long long)min(n + v, d_out - 1) * bld + j0);
+          for (int v = 0; v < 4; ++v) bq[v] = b8[j0 / 8 == 0 ? 0 : kPre - 1][v];
+        } else {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) bq[v] = ld16(Bb + (long long)min(n + v, d_out - 1) * bld + j0);
+        }
 #pragma unroll
         for (int v = 0; v < 4; ++v)
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const uint32_t wd = b8[v][e / 2];
+            const uint32_t wd = bq[v][e / 2];
             const float bv = bf16_bits_to_f32((uint16_t)((e & 1) ? (wd >> 16) : (wd & 0xffffu)));
-            lsum[v] = fmaf(bv, vv[j0 + e], lsum[v]);   // vv[j >= r] is 0
+            // columns j >= r of the padded B row are zero; v there is unused
+            lsum[v] = fmaf(bv, j0 + e < r ? vv[j0 + e] : 0.f, lsum[v]);
           }
       }
+      const float sc = __int_as_float(pe.z);
 #pragma unroll
-      for (int v = 0; v < 4; ++v) acc[v] += lsum[v];
+      for (int v = 0; v < 4; ++v) acc[v] += sc * lsum[v];
     }
   }
 
   if (t >= T) return;
-  int row = a.sv.token_index ? a.sv.token_index[t] : t;
   row = min(max(row, 0), T - 1);
   uint16_t* yr = (uint16_t*)a.y + (long long)row * d_out;
   if (n + 3 < d_out && (d_out & 3) == 0) {

@@ -43,6 +43,7 @@ struct DecodeArgs {
   PoolView pv;
   float* ypart;    // workspace: partial tiles [n_chunks][n_tiles][4][T/16 blocks][256]
   float* v_part;   // workspace: shrink partials [n_chunks][T][r_ws]
+  int4* pos;       // workspace: per sorted position {adapter or -1, rank, scale bits, 0} [T]
   int r_ws;
   int n_tiles;     // ceil(d_out / 64)
   int kc;          // d_in chunk width (multiple of 64)
