@@ -229,6 +229,7 @@ __global__ __launch_bounds__(256) void k_vfinal(LinearArgs a) {
 // ---------------------------------------------------------------------------
 constexpr int kGKB = 64;            // k per pipeline stage
 constexpr int kBatch = 8;           // independent loads per thread in bulk LDS copies
+constexpr int kEpiRing = 16;        // B operand loads in flight per lane in the expand epilogue
 constexpr int kGPitch = kGKB + 8;   // LDS row pitch in bf16 (144 bytes)
 
 template <int BR, int BT, int WR, int WT, int PD>
@@ -356,27 +357,20 @@ __global__ __launch_bounds__((BR / WR) * (BT / WT) * kWave) void k_gemm2(LinearA
   }
 
   // ---- expand: acc += B_a (scale v) per segment run, on MFMA ---------------
-  // Runs of one segment among the tile's positions are listed once, with each
-  // position's run index. Per rank chunk of up to 64 columns, scale*v of the
-  // tile's positions is staged in LDS already split into a bf16 high and low
-  // part; B slices (BR rows) of a group of runs are staged next to it, the
-  // next group's slices loading into registers while the current group's
-  // MFMAs run. A token block only visits the runs that overlap it.
+  // scale*v of the tile's positions is staged in LDS (per rank chunk of up to
+  // 64 columns), split into bf16 high and low parts so the MFMA keeps about
+  // 16 mantissa bits of v. Each wave then walks the segment runs of its own
+  // WT positions on its own, with no block barrier: a work unit is (run,
+  // 16 rank columns); the unit's B slice (the wave's WR rows) is loaded from
+  // the pool straight into MFMA operand registers, a ring of kEpiRing units
+  // ahead of the unit being multiplied.
   if (a.lora_on) {
-    constexpr int MAXP = 16;                         // B pieces per thread per group
     const int RC = a.r_ws < 64 ? a.r_ws : 64;        // rank columns per chunk (16, 32 or 64)
     const int VP = RC + 8;                           // hi/lo row pitch (bf16)
-    const int BP = RC + 8;                           // bs row pitch (bf16)
-    const int VS_BYTES = 2 * BT * VP * 2;
-    int G = (C::LDS_BYTES - VS_BYTES) / (BR * BP * 2);
-    G = min(G, MAXP * C::NT / (BR * (RC / 8)));      // runs per group (>= 1)
     uint16_t* vsh = lds;
     uint16_t* vsl = lds + BT * VP;
-    uint16_t* bs = lds + VS_BYTES / 2;
-    __shared__ int rstart[BT + 1];
-    __shared__ int prun[BT];
-    __shared__ int rflag[C::NT];
-    __shared__ int nrun;
+    constexpr int WRUNS = WT + 1;
+    __shared__ int wstart[C::NW][WRUNS];             // per-wave run starts (tile positions)
 
     const int teff = min(BT, T - t0);
     for (int t = tid; t < BT; t += C::NT) {
@@ -391,74 +385,24 @@ __global__ __launch_bounds__((BR / WR) * (BT / WT) * kWave) void k_gemm2(LinearA
       pinfo[t] = e;
     }
     __syncthreads();
-    {  // run list: thread t owns positions [t*PPT, t*PPT + PPT)
-      constexpr int PPT = (BT + C::NT - 1) / C::NT;
-      int cnt = 0;
-      for (int i = 0; i < PPT; ++i) {
-        const int t = tid * PPT + i;
-        if (t < teff && (t == 0 || pinfo[t].x != pinfo[t - 1].x)) ++cnt;
-      }
-      rflag[tid] = cnt;
-      __syncthreads();
-      for (int off = 1; off < C::NT; off <<= 1) {
-        const int v = tid >= off ? rflag[tid - off] : 0;
-        __syncthreads();
-        rflag[tid] += v;
-        __syncthreads();
-      }
-      int idx = rflag[tid] - cnt;
-      for (int i = 0; i < PPT; ++i) {
-        const int t = tid * PPT + i;
-        if (t < teff) {
-          if (t == 0 || pinfo[t].x != pinfo[t - 1].x) rstart[idx++] = t;
-          prun[t] = idx - 1;
-        }
-      }
-      if (tid == C::NT - 1) {
-        nrun = rflag[C::NT - 1];
-        rstart[rflag[C::NT - 1]] = teff;
-      }
-      __syncthreads();
+
+    // runs of this wave's positions [wb, we): a run starts where the segment changes
+    const int wb = wt * WT, we = min(wb + WT, teff);
+    int nrw = 0;                                     // runs of this wave (uniform)
+    for (int c0 = wb; c0 < we; c0 += kWave) {
+      const int t = c0 + lane;
+      const bool st = t < we && (t == wb || pinfo[t].x != pinfo[t - 1].x);
+      const unsigned long long m = __ballot(st);
+      if (st) wstart[wave][nrw + __popcll(m & ((1ull << lane) - 1ull))] = t;
+      nrw += __popcll(m);
     }
-    const int nr = nrun;
+    if (lane == 0) wstart[wave][nrw] = we;
+    // (wave-private table: the wave's own LDS writes are ordered before its reads)
 
-    // B pieces of group g0: run g0+g, row, 16-byte column q
-    u32x4_t bq[MAXP];
-    // rc: columns of the current chunk (a multiple of 16, at most RC)
-    auto load_b = [&](int jc0, int rc, int g0) {
-      const int ppr = BR * (rc / 8);                 // pieces per run
-      const int nbs = min(G, nr - g0) * ppr;
-#pragma unroll
-      for (int u = 0; u < MAXP; ++u) {
-        const int e = min(tid + u * C::NT, max(nbs - 1, 0));
-        const int g = e / ppr, rem = e % ppr;
-        const int row = rem / (rc / 8), q = rem % (rc / 8);
-        const int4 pi = pinfo[rstart[min(g0 + g, nr - 1)]];
-        const int j = jc0 + 8 * q;
-        const bool ok = nbs > 0 && pi.y >= 0 && j < pi.z;
-        // an absent slice reads the zero block (no select on the loaded value)
-        const uint16_t* src = ok ? (const uint16_t*)a.pv.base + (long long)pi.y * a.pv.slot_elems +
-                                       a.pv.b_offset + (long long)min(r0 + row, d_out - 1) * round_up8(pi.z) + j
-                                 : zeros;
-        bq[u] = ld16(src);
-      }
-    };
-    auto store_b = [&](int rc, int g0) {
-      const int ppr = BR * (rc / 8);
-      const int nbs = min(G, nr - g0) * ppr;
-#pragma unroll
-      for (int u = 0; u < MAXP; ++u) {
-        const int e = tid + u * C::NT;
-        if (e < nbs) {
-          const int g = e / ppr, rem = e % ppr;
-          *(u32x4_t*)&bs[(g * BR + rem / (rc / 8)) * BP + 8 * (rem % (rc / 8))] = bq[u];
-        }
-      }
-    };
-
+    constexpr int P = kEpiRing / C::MR;              // units in flight
     for (int jc0 = 0; jc0 < a.r_ws; jc0 += RC) {
       const int rc = min(RC, a.r_ws - jc0);
-      if (nr > 0) load_b(jc0, rc, 0);
+      if (jc0 > 0) __syncthreads();                  // previous chunk's v reads are done
       // scale * v of the tile's positions, split into bf16 high and low parts
       const int nvs = BT * (rc / 4);
       for (int e0 = tid; e0 < nvs; e0 += C::NT * kBatch) {
@@ -489,37 +433,72 @@ __global__ __launch_bounds__((BR / WR) * (BT / WT) * kWave) void k_gemm2(LinearA
           }
         }
       }
-      for (int g0 = 0; g0 < nr; g0 += G) {
-        store_b(rc, g0);
-        __syncthreads();
-        if (g0 + G < nr) load_b(jc0, rc, g0 + G);   // lands while the MFMAs below run
-        const int gend = min(g0 + G, nr) - 1;
+      __syncthreads();
+
+      // unit cursor (wave-uniform): run k of this wave, rank columns jc0 + jc
+      auto run_rank = [&](int k) {   // ranks of run k inside this chunk (0: no adapter term)
+        const int4 pi = pinfo[wstart[wave][k]];
+        return pi.y >= 0 ? min(pi.z - jc0, rc) : 0;
+      };
+      auto advance = [&](int& k, int& jc) {
+        jc += 16;
+        while (k < nrw && jc >= run_rank(k)) {
+          ++k;
+          jc = 0;
+        }
+      };
+      u32x4_t ring[P][C::MR];
+      int uk[P], ujc[P];
+      auto load_unit = [&](int slot, int k, int jc) {
+        const bool ok = k < nrw;
+        const int4 pi = pinfo[wstart[wave][ok ? k : 0]];
+        const int col = jc0 + jc + kh;
+        const bool live = ok && pi.y >= 0 && col < pi.z;
+        const uint16_t* bb = (const uint16_t*)a.pv.base + (long long)(live ? pi.y : 0) * a.pv.slot_elems +
+                             a.pv.b_offset;
+        const int pitch = round_up8(pi.z);
 #pragma unroll
-        for (int n = 0; n < C::MT; ++n) {
-          const int tb0 = wt * WT + n * 32;
-          if (tb0 >= teff) continue;                            // uniform
-          const int glo = max(prun[tb0], g0);
-          const int ghi = min(prun[min(tb0 + 31, teff - 1)], gend);
-          const int tl = tb0 + l32;
-          for (int g = glo; g <= ghi; ++g) {                    // uniform
-            const int rs = rstart[g], re = rstart[g + 1];
-            const int4 pi = pinfo[rs];
-            if (pi.y < 0) continue;
-            const bool in = tl >= rs && tl < re;
-            for (int jc = 0; jc < rc && jc0 + jc < pi.z; jc += 16) {
+        for (int m = 0; m < C::MR; ++m) {
+          const int row = min(r0 + wr * WR + m * 32 + l32, d_out - 1);
+          // columns past the adapter's rank read the zero block (no select)
+          ring[slot][m] = ld16(live ? bb + (long long)row * pitch + col : zeros);
+        }
+        uk[slot] = k;
+        ujc[slot] = jc;
+      };
+      int pk = 0, pjc = -16;
+      advance(pk, pjc);                              // first unit
+#pragma unroll
+      for (int u = 0; u < P; ++u) {
+        load_unit(u, pk, pjc);
+        advance(pk, pjc);
+      }
+      while (uk[0] < nrw) {                          // uniform
+#pragma unroll
+        for (int u = 0; u < P; ++u) {
+          const int k = uk[u], jc = ujc[u];
+          if (k < nrw) {                             // uniform
+            const int rs = wstart[wave][k], re = wstart[wave][k + 1];
+            // token blocks of this wave that the run covers
+            const int n_lo = (rs - wb) / 32, n_hi = (re - 1 - wb) / 32;
+#pragma unroll
+            for (int n = 0; n < C::MT; ++n) {
+              if (n < n_lo || n > n_hi) continue;    // uniform
+              const int tl = wb + n * 32 + l32;
+              const bool in = tl >= rs && tl < re;
               u32x4_t hiu = *(const u32x4_t*)&vsh[min(tl, BT - 1) * VP + jc + kh];
               u32x4_t lou = *(const u32x4_t*)&vsl[min(tl, BT - 1) * VP + jc + kh];
               if (!in) { hiu = zero_u32x4(); lou = zero_u32x4(); }
 #pragma unroll
               for (int m = 0; m < C::MR; ++m) {
-                const u32x4_t bop = *(const u32x4_t*)&bs[((g - g0) * BR + wr * WR + m * 32 + l32) * BP + jc + kh];
-                acc[m][n] = mfma32g(bop, hiu, acc[m][n]);
-                acc[m][n] = mfma32g(bop, lou, acc[m][n]);
+                acc[m][n] = mfma32g(ring[u][m], hiu, acc[m][n]);
+                acc[m][n] = mfma32g(ring[u][m], lou, acc[m][n]);
               }
             }
           }
+          load_unit(u, pk, pjc);                     // refill the slot P units ahead
+          advance(pk, pjc);
         }
-        __syncthreads();
       }
     }
   }
