@@ -6,7 +6,8 @@
 //
 //  k_shrink2  v = A_a x per segment, fp32, split over d_in chunks into
 //             deterministic partials; also writes a per-position table
-//             {segment, adapter, rank, scale} read by the GEMM epilogue.
+//             {segment, adapter, rank, scale}; k_vfinal folds the partials in
+//             chunk order and applies the scale (v_fin, read by the epilogue).
 //  k_gemm2    W x as a tiled GEMM on v_mfma_f32_32x32x16_bf16: block tile of
 //             BR W rows x BT sorted positions over the whole of d_in, both
 //             operands staged through LDS (double-buffered, 144-byte row pitch
@@ -34,29 +35,52 @@ __device__ __forceinline__ f32x16_t mfma32g(u32x4_t a, u32x4_t b, f32x16_t c) {
 // ---------------------------------------------------------------------------
 // Shrink. grid (items, d_in chunks), 4 waves. An item is one 64-position block
 // of one segment (segments longer than 64 positions give several items, so
-// long prefill segments spread over many workgroups). Each workgroup finds its
-// item with a scan of the segment starts in LDS. Chunk c covers k-steps
-// [c*nks/ks, (c+1)*nks/ks) of 32, walked in groups of 16 k-steps (512 d_in):
-// wave w takes k-steps w, w+4, w+8, w+12 of each group and accumulates in
-// registers; the four waves are summed in a fixed order through LDS.
-// MFMA rows = sorted positions (16 per block), columns = rank index j.
+// long prefill segments spread over many workgroups); each workgroup finds
+// its item with a scan of the segment starts in LDS, where the segments'
+// adapter ids and ranks are loaded in the same round, so the A loads can
+// start right after the scan (the pool's slot table is read alongside and
+// only decides the per-position table). Chunk c covers k-steps
+// [c*nks/ks, (c+1)*nks/ks) of 32; wave w takes every fourth k-step starting
+// at w, with a ring of D k-steps of operands in flight in registers. A
+// k-step loads NRB position blocks of x and NCB rank blocks of A (16 each):
+// the kernel is instantiated for the block counts the batch needs, so a
+// short, low-rank segment keeps a deep ring of useful loads. Absent operands
+// read the pool's zero block (every load is unconditional, no loaded value
+// is selected). The four waves are summed in a fixed order through LDS into
+// v_part[c][p][j] (unscaled). MFMA rows = positions, columns = rank index.
 // ---------------------------------------------------------------------------
-constexpr int kShrKs = 4;         // k-steps per wave per group
 constexpr int kShrMaxSeg = MLORA_MAX_SEGMENTS;  // segments the item scan handles
+constexpr int kShrLdsSeg = 4096;                // up to this many, adapters and ranks go to LDS too
 
+template <int NRB, int NCB>
 __global__ __launch_bounds__(256) void k_shrink2(LinearArgs a) {
+  constexpr int D = 16 / (NRB + NCB);   // k-steps in flight per wave (<= 64 operand VGPRs)
+  constexpr int NQ = NRB * NCB * 4;     // accumulator floats per lane
   const int item = blockIdx.x, c = blockIdx.y;
   const SegView& sv = a.sv;
   const int S = min(seg_count(sv), kShrMaxSeg);
   const int T = a.T, d_in = a.d_in;
   const int tid = threadIdx.x;
-  extern __shared__ int sst[];   // [S + 1] segment starts (dynamic LDS)
-  __shared__ int part[256];
+  const int wave = tid / kWave, lane = tid % kWave;
+  // segment starts [S + 1], and (S <= kShrLdsSeg) the adapters [S] and ranks [S]
+  extern __shared__ int sdyn[];
+  const bool meta_lds = S <= kShrLdsSeg;
+  int* sst = sdyn;
+  int* sad = sdyn + S + 1;
+  int* srk = sdyn + 2 * S + 1;
+  __shared__ int wsum[4];
   __shared__ int found[2];
-  __shared__ float red[4][kWave][17];
+  __shared__ float red[4][kWave][NQ + 1];
 
   // ---- which (segment, block) is this item? --------------------------------
-  for (int i = tid; i <= S; i += 256) sst[i] = sv.seg_start[i];
+  for (int i = tid; i <= S; i += 256) {
+    sst[i] = sv.seg_start[i];
+    if (meta_lds && i < S) {
+      sad[i] = sv.seg_adapter[i];
+      srk[i] = sv.seg_rank ? sv.seg_rank[i] : 0;
+    }
+  }
+  if (tid == 0) found[0] = -1;
   __syncthreads();
   const int per = (S + 255) / 256;
   int cnt = 0;
@@ -64,19 +88,18 @@ __global__ __launch_bounds__(256) void k_shrink2(LinearArgs a) {
     const int len = min(sst[i + 1], T) - max(sst[i], 0);
     cnt += len > 0 ? (len + 63) / 64 : 0;
   }
-  part[tid] = cnt;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    const int v = tid >= off ? part[tid - off] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
+  int inc = cnt;   // inclusive scan: wave, then the waves before it
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int up = __shfl_up(inc, off, kWave);
+    if (lane >= off) inc += up;
   }
-  if (tid == 0) found[0] = -1;
+  if (lane == kWave - 1) wsum[wave] = inc;
   __syncthreads();
+  for (int w = 0; w < wave; ++w) inc += wsum[w];
   {
-    const int lo = part[tid] - cnt;   // items before this thread's segments
-    if (item >= lo && item < part[tid]) {
+    const int lo = inc - cnt;   // items before this thread's segments
+    if (item >= lo && item < inc) {
       int acc = lo;
       for (int i = tid * per; i < min(S, tid * per + per); ++i) {
         const int len = min(sst[i + 1], T) - max(sst[i], 0);
@@ -95,106 +118,112 @@ __global__ __launch_bounds__(256) void k_shrink2(LinearArgs a) {
   if (s < 0) return;   // uniform: past the last item
   const int ps = max(sst[s], 0) + 64 * found[1];
   const int pe = min(min(sst[s + 1], T), ps + 64);
-  int r;
-  const int ad = seg_adapter_checked(sv, a.pv, s, &r);
-  if (c == 0) {   // per-position table for the GEMM epilogue
-    const float scl = ad >= 0 ? sv.seg_scale[s] : 0.f;
-    for (int p = ps + tid; p < pe; p += 256) {
-      int4 e;
-      e.x = s;
-      e.y = ad;
-      e.z = ad >= 0 ? r : 0;
-      e.w = __float_as_int(scl);
-      a.pos_info[p] = e;
-    }
+  // adapter and A rows to read: the segment's own id and rank, clamped into
+  // the pool; the slot table (registration) is applied to the position table
+  const int ad0 = meta_lds ? sad[s] : sv.seg_adapter[s];
+  const int rk0 = meta_lds ? srk[s] : (sv.seg_rank ? sv.seg_rank[s] : 0);
+  const bool adok = ad0 >= 0 && ad0 < a.pv.capacity;
+  const int ra = adok ? min(max(rk0, 0), a.pv.max_rank) : 0;
+  const int reg_rank = a.pv.rank[adok ? ad0 : 0];
+  const float scl = sv.seg_scale[s];
+  auto write_pos = [&]() {
+    if (c != 0) return;
+    const int r = adok && reg_rank > 0 && ra > 0 ? min(ra, reg_rank) : 0;
+    const int ad = r > 0 ? ad0 : -1;
+    for (int p = ps + tid; p < pe; p += 256) a.pos_info[p] = make_int4(s, ad, r, __float_as_int(r > 0 ? scl : 0.f));
+  };
+  if (ra == 0) {
+    write_pos();
+    return;
   }
-  if (ad < 0) return;
 
   const uint16_t* __restrict__ x = (const uint16_t*)a.x;
-  const uint16_t* __restrict__ Aa = (const uint16_t*)a.pv.base + (long long)ad * a.pv.slot_elems;
+  const uint16_t* __restrict__ Aa = (const uint16_t*)a.pv.base + (long long)ad0 * a.pv.slot_elems;
+  const uint16_t* zeros = (const uint16_t*)a.pv.zeros;
   const int nks = (d_in + 31) / 32;
   const int kb = (int)((long long)c * nks / a.ks);
   const int ke = (int)((long long)(c + 1) * nks / a.ks);
-  const int wave = tid / kWave, lane = tid % kWave;
+  const int nst = (ke - kb - wave + 3) / 4;            // this wave's k-steps
+  const int nst_w = (ke - kb + 3) / 4;                 // wave 0's (the most); uniform loop bound
+  const int nst_pad = (nst_w + D - 1) / D * D;
   const int l16 = lane % 16, kq = 8 * (lane / 16);
 
-  // x rows of the block's positions (fixed over k)
-  const uint16_t* xrow[4];
-  bool pval[4];
+  for (int pg = ps; pg < pe; pg += 16 * NRB) {
+    // x rows of this position group (fixed over k); absent positions read zeros
+    const uint16_t* xrow[NRB];
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-    const int p = ps + rb * 16 + l16;
-    pval[rb] = p < pe;
-    int row = sv.token_index ? sv.token_index[pval[rb] ? p : ps] : (pval[rb] ? p : ps);
-    row = min(max(row, 0), T - 1);
-    xrow[rb] = x + (long long)row * d_in;
-  }
-
-  for (int jg = 0; jg < r; jg += 64) {
-    f32x4_t acc[4][4];
+    for (int rb = 0; rb < NRB; ++rb) {
+      const int p = pg + rb * 16 + l16;
+      int row = p < pe ? (sv.token_index ? sv.token_index[p] : p) : 0;
+      row = min(max(row, 0), T - 1);
+      xrow[rb] = p < pe ? x + (long long)row * d_in : nullptr;
+    }
+    const int nrb = min(NRB, (pe - pg + 15) / 16);
+    for (int jg = 0; jg < ra; jg += 16 * NCB) {
+      const uint16_t* arow[NCB];
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int kg = kb; kg < ke; kg += 4 * kShrKs) {
-      int koff[kShrKs];
-      bool kval[kShrKs];
-#pragma unroll
-      for (int i = 0; i < kShrKs; ++i) {
-        const int ks = kg + wave + 4 * i;
-        kval[i] = ks < ke && ks * 32 + kq < d_in;
-        koff[i] = kval[i] ? ks * 32 + kq : 0;
-      }
-      u32x4_t af[4][kShrKs], xf[4][kShrKs];
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
+      for (int cb = 0; cb < NCB; ++cb) {
         const int j = jg + cb * 16 + l16;
-        const bool jv = j < r;
-        const uint16_t* arow = Aa + (long long)(jv ? j : 0) * d_in;
+        arow[cb] = j < ra ? Aa + (long long)j * d_in : nullptr;
+      }
+      const int ncb = min(NCB, (ra - jg + 15) / 16);
+      f32x4_t acc[NRB][NCB];
 #pragma unroll
-        for (int i = 0; i < kShrKs; ++i) {
-          const u32x4_t v = ld16(arow + koff[i]);
-          af[cb][i] = (jv && kval[i]) ? v : zero_u32x4();
+      for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) acc[rb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      u32x4_t af[D][NCB], xf[D][NRB];
+      auto load = [&](int slot, int i) {   // this wave's i-th k-step
+        const int k = (kb + wave + 4 * i) * 32 + kq;
+        const bool kin = i < nst && k < d_in;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) af[slot][cb] = ld16(kin && arow[cb] ? arow[cb] + k : zeros + kq);
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) xf[slot][rb] = ld16(kin && xrow[rb] ? xrow[rb] + k : zeros + kq);
+      };
+#pragma unroll
+      for (int u = 0; u < D; ++u) load(u, u);
+      for (int i0 = 0; i0 < nst_pad; i0 += D) {
+#pragma unroll
+        for (int u = 0; u < D; ++u) {
+#pragma unroll
+          for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+              if (rb < nrb && cb < ncb) acc[rb][cb] = mfma16g(xf[u][rb], af[u][cb], acc[rb][cb]);
+          load(u, i0 + u + D);   // past the end: zero-block reads
         }
       }
+      // fixed-order sum of the four waves, spread over all threads: entry
+      // e = (q, l) is accumulator value q of lane l
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
+      for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
-        for (int i = 0; i < kShrKs; ++i) {
-          const u32x4_t v = ld16(xrow[rb] + koff[i]);
-          xf[rb][i] = (pval[rb] && kval[i]) ? v : zero_u32x4();
-        }
+        for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-      for (int i = 0; i < kShrKs; ++i)
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-          for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = mfma16g(xf[rb][i], af[cb][i], acc[rb][cb]);
-    }
-    // fixed-order sum of the four waves, one 16-position block at a time
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      if (ps + rb * 16 >= pe) break;   // uniform
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) red[wave][lane][cb * 4 + v] = acc[rb][cb][v];
+          for (int v = 0; v < 4; ++v) red[wave][lane][(rb * NCB + cb) * 4 + v] = acc[rb][cb][v];
       __syncthreads();
-      for (int e = tid; e < kWave * 16; e += 256) {
-        const int l = e / 16, q = e % 16, cb = q / 4, v = q % 4;
-        const int p = ps + rb * 16 + 4 * (l / 16) + v;
-        const int j = jg + cb * 16 + (l % 16);
-        const float sum = ((red[0][l][q] + red[1][l][q]) + red[2][l][q]) + red[3][l][q];
-        if (p < pe && j < r) a.v_part[((long long)c * T + p) * a.r_ws + j] = sum;
+      for (int e = tid; e < NQ * kWave; e += 256) {
+        const int q = e / kWave, l = e % kWave;
+        const int rb = q / (NCB * 4), cb = (q / 4) % NCB, v = q % 4;
+        if (rb < nrb && cb < ncb) {
+          const float sum = ((red[0][l][q] + red[1][l][q]) + red[2][l][q]) + red[3][l][q];
+          const int p = pg + rb * 16 + 4 * (l / 16) + v;
+          const int j = jg + cb * 16 + (l % 16);
+          if (p < pe && j < ra) a.v_part[((long long)c * T + p) * a.r_ws + j] = sum;
+        }
       }
       __syncthreads();
     }
   }
+  write_pos();
 }
 
 // ---------------------------------------------------------------------------
 // Finalize: v_fin[p][j] = scale_p * sum_c v_part[c][p][j] (chunk order) for
-// j < rank_p, else 0. One thread per 4 rank columns of one position.
+// j < rank_p, else 0. One thread per 4 rank columns of one position; all the
+// chunk loads are in flight at once. Every row tile of the GEMM then reads
+// one v per position instead of re-reading the chunk partials.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_vfinal(LinearArgs a) {
   const int e = blockIdx.x * 256 + threadIdx.x;
@@ -205,12 +234,12 @@ __global__ __launch_bounds__(256) void k_vfinal(LinearArgs a) {
   const int rk = (pi.y >= 0 && pi.y < a.pv.capacity) ? min(pi.z, a.pv.max_rank) : 0;
   f32x4_t sum = f32x4_t{0.f, 0.f, 0.f, 0.f};
   if (j < rk) {
-    f32x4_t part[8];
+    f32x4_t part[kMaxShrinkSplit];
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
+    for (int c = 0; c < kMaxShrinkSplit; ++c)
       part[c] = *(const f32x4_t*)(a.v_part + ((long long)min(c, a.ks - 1) * a.T + p) * a.r_ws + j);
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
+    for (int c = 0; c < kMaxShrinkSplit; ++c)
       if (c < a.ks) {
         sum[0] += part[c][0];
         sum[1] += part[c][1];
@@ -230,6 +259,7 @@ __global__ __launch_bounds__(256) void k_vfinal(LinearArgs a) {
 constexpr int kGKB = 64;            // k per pipeline stage
 constexpr int kBatch = 8;           // independent loads per thread in bulk LDS copies
 constexpr int kEpiRing = 16;        // B operand loads in flight per lane in the expand epilogue
+constexpr int kEpiMaxUnits = 128;   // work units one wave lists per rank chunk (more: further passes)
 constexpr int kGPitch = kGKB + 8;   // LDS row pitch in bf16 (144 bytes)
 
 template <int BR, int BT, int WR, int WT, int PD>
@@ -253,7 +283,8 @@ __global__ __launch_bounds__((BR / WR) * (BT / WT) * kWave) void k_gemm2(LinearA
   __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_BYTES / 2];
   __shared__ int4 pinfo[BT];
 
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  // wave index made scalar: every per-wave quantity below is then uniform
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
   const int l32 = lane % 32, kh = 8 * (lane / 32);
   const int T = a.T, d_in = a.d_in, d_out = a.d_out;
   const int n_rt = (d_out + BR - 1) / BR;
@@ -371,6 +402,7 @@ __global__ __launch_bounds__((BR / WR) * (BT / WT) * kWave) void k_gemm2(LinearA
     uint16_t* vsl = lds + BT * VP;
     constexpr int WRUNS = WT + 1;
     __shared__ int wstart[C::NW][WRUNS];             // per-wave run starts (tile positions)
+    __shared__ int4 udesc[C::NW][kEpiMaxUnits];      // per-wave work units of a rank chunk
 
     const int teff = min(BT, T - t0);
     for (int t = tid; t < BT; t += C::NT) {
@@ -396,6 +428,7 @@ __global__ __launch_bounds__((BR / WR) * (BT / WT) * kWave) void k_gemm2(LinearA
       if (st) wstart[wave][nrw + __popcll(m & ((1ull << lane) - 1ull))] = t;
       nrw += __popcll(m);
     }
+    nrw = __builtin_amdgcn_readfirstlane(nrw);
     if (lane == 0) wstart[wave][nrw] = we;
     // (wave-private table: the wave's own LDS writes are ordered before its reads)
 
@@ -435,60 +468,100 @@ __global__ __launch_bounds__((BR / WR) * (BT / WT) * kWave) void k_gemm2(LinearA
       }
       __syncthreads();
 
-      // unit cursor (wave-uniform): run k of this wave, rank columns jc0 + jc
-      auto run_rank = [&](int k) {   // ranks of run k inside this chunk (0: no adapter term)
-        const int4 pi = pinfo[wstart[wave][k]];
-        return pi.y >= 0 ? min(pi.z - jc0, rc) : 0;
-      };
-      auto advance = [&](int& k, int& jc) {
-        jc += 16;
-        while (k < nrw && jc >= run_rank(k)) {
-          ++k;
-          jc = 0;
+      // unit list of this wave (wave-private LDS), built in parallel: lane l
+      // takes run k0 + l and writes one descriptor per 16 rank columns it has
+      // in this chunk: {rs | re << 16, jc, adapter, B row pitch}. A pass
+      // lists at most kEpiMaxUnits units; longer lists take further passes.
+      for (int pb = 0;; pb += kEpiMaxUnits) {
+      int nu_tot = 0;                                // units of the chunk (uniform)
+      for (int k0 = 0; k0 < nrw; k0 += kWave) {
+        const int k = k0 + lane;
+        int rs = 0, re = 0, ad = -1, pitch = 0, cnt = 0;
+        if (k < nrw) {
+          rs = wstart[wave][k];
+          re = wstart[wave][k + 1];
+          const int4 pi = pinfo[rs];
+          const int rk = pi.y >= 0 ? min(pi.z - jc0, rc) : 0;
+          cnt = rk > 0 ? (rk + 15) / 16 : 0;
+          ad = pi.y;
+          pitch = round_up8(pi.z);
         }
+        int inc = cnt;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+          const int up = __shfl_up(inc, off, kWave);
+          if (lane >= off) inc += up;
+        }
+        const int base = nu_tot + inc - cnt;
+        for (int i = 0; i < cnt; ++i) {
+          const int g = base + i - pb;
+          if (g >= 0 && g < kEpiMaxUnits) udesc[wave][g] = make_int4(rs | (re << 16), 16 * i, ad, pitch);
+        }
+        nu_tot += __builtin_amdgcn_readfirstlane(__shfl(inc, kWave - 1, kWave));
+      }
+      const int nu = min(nu_tot - pb, kEpiMaxUnits);
+
+      // A unit's descriptor is read from LDS (all lanes the same address) and
+      // made scalar with readfirstlane, so the unit loop branches and forms
+      // the B slice's base address on the scalar unit; the read for the unit
+      // refilled next is issued before the current unit's MFMAs.
+      auto sdesc = [&](int4 dv) {
+        return make_int4(__builtin_amdgcn_readfirstlane(dv.x), __builtin_amdgcn_readfirstlane(dv.y),
+                         __builtin_amdgcn_readfirstlane(dv.z), __builtin_amdgcn_readfirstlane(dv.w));
+      };
+      auto rdesc = [&](int u) {   // u uniform; past the list: any entry (not used)
+        return udesc[wave][min(u, kEpiMaxUnits - 1)];
       };
       u32x4_t ring[P][C::MR];
-      int uk[P], ujc[P];
-      auto load_unit = [&](int slot, int k, int jc) {
-        const bool ok = k < nrw;
-        const int4 pi = pinfo[wstart[wave][ok ? k : 0]];
-        const int col = jc0 + jc + kh;
-        const bool live = ok && pi.y >= 0 && col < pi.z;
-        const uint16_t* bb = (const uint16_t*)a.pv.base + (long long)(live ? pi.y : 0) * a.pv.slot_elems +
-                             a.pv.b_offset;
-        const int pitch = round_up8(pi.z);
+      const int rowb = r0 + wr * WR;                 // first row of this wave
+      auto load_unit = [&](int slot, int4 d, bool ok) {   // d scalar
+        const bool live = ok && d.z >= 0;
+        const uint16_t* sb = (const uint16_t*)a.pv.base +
+                             (live ? (long long)d.z * a.pv.slot_elems + a.pv.b_offset + jc0 + d.y : 0);
+        const int col = jc0 + d.y + kh;
 #pragma unroll
         for (int m = 0; m < C::MR; ++m) {
-          const int row = min(r0 + wr * WR + m * 32 + l32, d_out - 1);
-          // columns past the adapter's rank read the zero block (no select)
-          ring[slot][m] = ld16(live ? bb + (long long)row * pitch + col : zeros);
+          const int row = min(rowb + m * 32 + l32, d_out - 1);
+          // columns past the adapter's rank read the zero block (no select):
+          // col < rank implies col + 8 <= the padded row pitch d.w
+          ring[slot][m] = ld16(live && col < d.w ? sb + (long long)row * d.w + kh : zeros);
         }
-        uk[slot] = k;
-        ujc[slot] = jc;
       };
-      int pk = 0, pjc = -16;
-      advance(pk, pjc);                              // first unit
+      // v operands of a unit, one unit ahead (double buffer); the mask of
+      // positions outside the run is applied only where the MFMA uses them
+      u32x4_t vhi[2][C::MT], vlo[2][C::MT];
+      auto load_v = [&](int b, int jc) {
+#pragma unroll
+        for (int n = 0; n < C::MT; ++n) {
+          const int tl = min(wb + n * 32 + l32, BT - 1);
+          vhi[b][n] = *(const u32x4_t*)&vsh[tl * VP + jc + kh];
+          vlo[b][n] = *(const u32x4_t*)&vsl[tl * VP + jc + kh];
+        }
+      };
+      int4 dcur[P];
 #pragma unroll
       for (int u = 0; u < P; ++u) {
-        load_unit(u, pk, pjc);
-        advance(pk, pjc);
+        dcur[u] = sdesc(rdesc(u));
+        load_unit(u, dcur[u], u < nu);
       }
-      while (uk[0] < nrw) {                          // uniform
+      load_v(0, dcur[0].y);
+      for (int u0 = 0; u0 < nu; u0 += P) {          // uniform
 #pragma unroll
         for (int u = 0; u < P; ++u) {
-          const int k = uk[u], jc = ujc[u];
-          if (k < nrw) {                             // uniform
-            const int rs = wstart[wave][k], re = wstart[wave][k + 1];
-            // token blocks of this wave that the run covers
+          const int U = u0 + u;
+          const int4 d = dcur[u];
+          const int4 dnext = rdesc(U + P);           // LDS read in flight during the MFMAs
+          load_v((u + 1) & 1, dcur[(u + 1) % P].y);
+          if (U < nu) {                              // uniform (scalar)
+            const int rs = d.x & 0xffff, re = d.x >> 16;
             const int n_lo = (rs - wb) / 32, n_hi = (re - 1 - wb) / 32;
 #pragma unroll
             for (int n = 0; n < C::MT; ++n) {
               if (n < n_lo || n > n_hi) continue;    // uniform
               const int tl = wb + n * 32 + l32;
               const bool in = tl >= rs && tl < re;
-              u32x4_t hiu = *(const u32x4_t*)&vsh[min(tl, BT - 1) * VP + jc + kh];
-              u32x4_t lou = *(const u32x4_t*)&vsl[min(tl, BT - 1) * VP + jc + kh];
-              if (!in) { hiu = zero_u32x4(); lou = zero_u32x4(); }
+              const u32x4_t hiu = in ? vhi[u & 1][n] : zero_u32x4();
+              const u32x4_t lou = in ? vlo[u & 1][n] : zero_u32x4();
 #pragma unroll
               for (int m = 0; m < C::MR; ++m) {
                 acc[m][n] = mfma32g(ring[u][m], hiu, acc[m][n]);
@@ -496,9 +569,11 @@ __global__ __launch_bounds__((BR / WR) * (BT / WT) * kWave) void k_gemm2(LinearA
               }
             }
           }
-          load_unit(u, pk, pjc);                     // refill the slot P units ahead
-          advance(pk, pjc);
+          dcur[u] = sdesc(dnext);
+          load_unit(u, dcur[u], U + P < nu);        // refill the slot P units ahead
         }
+      }
+      if (pb + kEpiMaxUnits >= nu_tot) break;       // uniform
       }
     }
   }
@@ -543,7 +618,7 @@ __global__ __launch_bounds__((BR / WR) * (BT / WT) * kWave) void k_gemm2(LinearA
 int choose_shrink_split_bf16(int d_in, int items) {
   const int groups = (d_in + 511) / 512;
   int ks = 1;
-  while (ks < 8 && ks * 2 <= groups && items * ks < 512) ks *= 2;
+  while (ks < kMaxShrinkSplit && ks * 2 <= groups && items * ks < 1024) ks *= 2;
   return ks;
 }
 
@@ -563,9 +638,22 @@ static void launch_g(const LinearArgs& a, hipStream_t st) {
 // per CU) with as few W rows as keep the CUs busy.
 void launch_linear_bf16(const LinearArgs& a, hipStream_t st) {
   if (a.lora_on && a.seg_grid > 0) {
+    // block counts of the shrink: ranks up to the pool's (at most 64 per
+    // pass) and 16 or 64 positions per pass, by the batch's mean segment length
     const int nseg = a.seg_grid < kShrMaxSeg ? a.seg_grid : kShrMaxSeg;
-    hipLaunchKernelGGL(k_shrink2, dim3(shrink_items_bound(a.T, a.seg_grid), a.ks), dim3(256),
-                       (size_t)(nseg + 1) * sizeof(int), st, a);
+    const int rmax = a.pv.max_rank < 64 ? a.pv.max_rank : 64;
+    const bool long_segs = a.T > 16 * a.seg_grid;
+    const dim3 grid(shrink_items_bound(a.T, a.seg_grid), a.ks);
+    const size_t lds = (size_t)(nseg <= kShrLdsSeg ? 3 * nseg + 1 : nseg + 1) * sizeof(int);
+    if (long_segs) {
+      if (rmax <= 16) hipLaunchKernelGGL((k_shrink2<4, 1>), grid, dim3(256), lds, st, a);
+      else if (rmax <= 32) hipLaunchKernelGGL((k_shrink2<4, 2>), grid, dim3(256), lds, st, a);
+      else hipLaunchKernelGGL((k_shrink2<4, 4>), grid, dim3(256), lds, st, a);
+    } else {
+      if (rmax <= 16) hipLaunchKernelGGL((k_shrink2<1, 1>), grid, dim3(256), lds, st, a);
+      else if (rmax <= 32) hipLaunchKernelGGL((k_shrink2<1, 2>), grid, dim3(256), lds, st, a);
+      else hipLaunchKernelGGL((k_shrink2<1, 4>), grid, dim3(256), lds, st, a);
+    }
     const int n4 = a.T * (a.r_ws / 4);
     hipLaunchKernelGGL(k_vfinal, dim3((n4 + 255) / 256), dim3(256), 0, st, a);
   }

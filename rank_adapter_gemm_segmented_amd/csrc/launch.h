@@ -19,8 +19,8 @@ struct LinearArgs {
   SegView sv;
   PoolView pv;
   float* v_part;   // workspace: shrink partials [ks][T][r_ws] fp32
-  int4* pos_info;  // workspace: per sorted position {segment, adapter, rank, scale bits}
   float* v_fin;    // workspace: scale * v per sorted position [T][r_ws] fp32
+  int4* pos_info;  // workspace: per sorted position {segment, adapter, rank, scale bits}
   int r_ws;        // row pitch of v_part (max_rank rounded up to 16)
   int ks;          // number of d_in chunks of the shrink (1..kMaxShrinkSplit)
   int seg_grid;    // number of segments to cover (upper bound)
