@@ -438,6 +438,26 @@ __global__ __launch_bounds__(256) void k_finish_bf16(DecodeArgs a) {
     for (int v = 0; v < 4; ++v)
       b8[g][v] = ld16(Bb + (live ? (long long)min(n + v, d_out - 1) * bld + min(8 * g, bld - 8) : 0));
 
+  // v of the 16 tokens: sum of the stream kernel's slices [c][w]. A 16-byte
+  // quad of one token is element e; G groups of threads each sum every G-th
+  // slice of an element, then the groups are added in group order. The first
+  // batch of slice loads is issued here, with the partials still in flight.
+  const int nq = a.r_ws / 4;
+  const int E = 16 * nq;
+  const int G = E >= 256 ? 1 : E >= 128 ? 2 : 4;
+  const int nsl = a.n_chunks * kDecWaves;
+  const long long vstride = (long long)T * a.r_ws;
+  auto vptr = [&](int e0) {
+    const int e = min(e0 + tid / G, E - 1);
+    return a.v_part + (long long)min(tb * 16 + e / nq, T - 1) * a.r_ws + 4 * (e % nq);
+  };
+  f32x4_t vq[kFinUnroll];
+  if (lora) {
+    const float* vp = vptr(0);
+#pragma unroll
+    for (int u = 0; u < kFinUnroll; ++u) vq[u] = *(const f32x4_t*)(vp + min(tid % G + u * G, nsl - 1) * vstride);
+  }
+
   // chunk partials summed in chunk order
   f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -462,30 +482,22 @@ __global__ __launch_bounds__(256) void k_finish_bf16(DecodeArgs a) {
   }
 
   if (lora) {
-    // v of the 16 tokens: sum of the stream kernel's slices [c][w]. A 16-byte
-    // quad of one token is element e; G groups of threads each sum every G-th
-    // slice of an element, then the groups are added in group order.
-    const int nq = a.r_ws / 4;
-    const int E = 16 * nq;
-    const int G = E >= 256 ? 1 : E >= 128 ? 2 : 4;
-    const int nsl = a.n_chunks * kDecWaves;
-    const long long vstride = (long long)T * a.r_ws;
     for (int e0 = 0; e0 < E; e0 += 256 / G) {
-      const int g = tid % G, e = e0 + tid / G;
-      const int ti = min(e, E - 1) / nq, jq = min(e, E - 1) % nq;
-      const float* vp = a.v_part + (long long)min(tb * 16 + ti, T - 1) * a.r_ws + 4 * jq;
+      const int g = tid % G;
+      const float* vp = vptr(e0);
       f32x4_t sum = f32x4_t{0.f, 0.f, 0.f, 0.f};
       for (int s0 = g; s0 < nsl; s0 += G * kFinUnroll) {
-        f32x4_t q[kFinUnroll];
+        if (e0 > 0 || s0 > g) {
 #pragma unroll
-        for (int u = 0; u < kFinUnroll; ++u) q[u] = *(const f32x4_t*)(vp + min(s0 + u * G, nsl - 1) * vstride);
+          for (int u = 0; u < kFinUnroll; ++u) vq[u] = *(const f32x4_t*)(vp + min(s0 + u * G, nsl - 1) * vstride);
+        }
 #pragma unroll
         for (int u = 0; u < kFinUnroll; ++u)
           if (s0 + u * G < nsl) {
-            sum[0] += q[u][0];
-            sum[1] += q[u][1];
-            sum[2] += q[u][2];
-            sum[3] += q[u][3];
+            sum[0] += vq[u][0];
+            sum[1] += vq[u][1];
+            sum[2] += vq[u][2];
+            sum[3] += vq[u][3];
           }
       }
       vgrp[g][tid / G] = sum;
