@@ -82,14 +82,15 @@ def ingest_counters(workload: str, kernels, fetch_csv: str, write_csv: str) -> d
     """HBM traffic per layer call from two rocprofv3 --pmc runs of --profile.
 
     Each counter is scaled by what it reads for the calibration copy of
-    CALIB_BYTES (the largest __amd_rocclr_copyBuffer dispatch: it reads and
-    writes CALIB_BYTES). The layer's kernels are averaged over their LoRA-on
+    CALIB_BYTES (the last __amd_rocclr_copyBuffer dispatch of the run: it
+    reads and writes CALIB_BYTES). The layer's kernels are averaged over their LoRA-on
     dispatches and summed."""
     import csv
 
-    def per_kernel(path):
+    def per_kernel(path):   # values per kernel name, in dispatch order
+        rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Dispatch_Id"]))
         vals = {}
-        for r in csv.DictReader(open(path)):
+        for r in rows:
             vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
         return vals
 
@@ -97,7 +98,8 @@ def ingest_counters(workload: str, kernels, fetch_csv: str, write_csv: str) -> d
     total = 0.0
     for key, path in (("fetch", fetch_csv), ("write", write_csv)):
         vals = per_kernel(path)
-        calib = max(vals.get("__amd_rocclr_copyBuffer", [0.0]))
+        # the calibration copy is the run's last device copy
+        calib = vals.get("__amd_rocclr_copyBuffer", [0.0])[-1]
         if calib <= 0:
             raise SystemExit(f"{path}: no calibration copy found")
         factor = CALIB_BYTES / (calib * 1024.0)
