@@ -131,7 +131,7 @@ int run_linear(const void* x, const void* W, mlora_pool_s* pool, const SegView& 
   a.seg_grid = lora_on ? sv.n_seg : 0;
   if (pool->dtype == MLORA_BF16) {
     const int fp = forced_path();
-    const bool dec_ok = decode_supported(T, lora_on ? sv.n_seg : 0);
+    const bool dec_ok = decode_supported(T, lora_on ? sv.n_seg : 0, pool->d_out, pool->max_rank);
     if (dec_ok && fp != 2) {
       DecodeArgs d;
       d.x = x;
@@ -148,6 +148,7 @@ int run_linear(const void* x, const void* W, mlora_pool_s* pool, const SegView& 
       d.pos = a.pos_info;
       d.r_ws = a.r_ws;
       decode_plan(pool->d_in, pool->d_out, &d.n_tiles, &d.kc, &d.n_chunks);
+      d.unit_rows = decode_unit_rows(lora_on ? sv.n_seg : 0, pool->max_rank, d.n_tiles);
       launch_decode_bf16(d, stream);
       return check_launch();
     }

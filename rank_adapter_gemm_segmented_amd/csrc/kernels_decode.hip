@@ -11,11 +11,11 @@
 //  k_stream  one-shot items (n-tile of 64 W rows, d_in chunk c). An item loads
 //            its x chunk into LDS and its W rows straight into MFMA operand
 //            registers, every load in flight at once, then runs
-//            v_mfma_f32_16x16x32_bf16. The shrink v = A_a x is folded in as
-//            extra rows: the touched adapters' A rows (restricted to chunk c)
-//            are spread evenly over the items of chunk c and multiplied
-//            against the same x chunk in LDS. Outputs: fp32 partial tiles of
-//            W x and of v, one slot per chunk (deterministic, no atomics).
+//            v_mfma_f32_16x16x32_bf16. The shrink v = A_a x is folded in per
+//            segment: item (c, tile) takes segments tile, tile + n_tiles, ...
+//            and multiplies their A rows (restricted to chunk c) against the
+//            same x chunk in LDS. Outputs: fp32 partial tiles of W x and of
+//            v, one slot per chunk (deterministic, no atomics).
 //  k_finish  y = sum_c partial_c + scale_s * B_a (sum_c v_c), summed in chunk
 //            order, the expand on the vector ALUs in fp32, one bf16 store.
 //
@@ -36,19 +36,13 @@ constexpr int kDecWaves = kDecThreads / kWave;
 constexpr int kDecRows = 64;                       // W rows per item (4 blocks of 16)
 constexpr int kDecXPitch = kDecMaxKc + 8;          // LDS row pitch of the x chunk (bf16)
 constexpr int kDecWSteps = kDecMaxKc / 2 / 32;     // 32-wide k-steps per wave (16)
-constexpr int kDecWPre = 8;                        // W k-steps requested before the MFMA loop
-constexpr int kDecRowWin = 32;                     // shrink rows per item found by table lookup
+constexpr int kDecWPre = 8;                        // W k-steps requested before the x barrier
 constexpr int kDecASteps = kDecMaxKc / 8 / 32;     // shrink k-steps per wave per row block (4)
 
 template <int TT>
 struct DecSmem {
   uint16_t xs[TT * kDecXPitch];
   float red[4][kWave][4 * (TT / 16)];              // second-half partials of the W rows
-  int pref[kDecMaxSeg + 1];                        // shrink-row prefix over segments
-  int sad[kDecMaxSeg];                             // adapter of each segment (-1: none)
-  int sps[kDecMaxSeg], spe[kDecMaxSeg];            // token range of each segment
-  int rseg[kDecRowWin], rj[kDecRowWin];            // item's first shrink rows: segment, rank row
-  int posseg[64];                                  // segment of each sorted position (-1: none)
 };
 
 // Partial tile layout (fragment-major): for chunk c, n-tile i, row block rb,
@@ -57,20 +51,18 @@ __device__ __forceinline__ long long part_off(int c, int i, int rb, int tb, int 
   return ((((long long)c * n_tiles + i) * 4 + rb) * ntb + tb) * 256;
 }
 
-// segment s holding shrink row q (pref is non-decreasing, pref[0] = 0 <= q)
-__device__ __forceinline__ int seg_of_row(const int* pref, int nseg, int q) {
-  int lo = 0, hi = nseg - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (pref[mid] <= q) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
-
 // Loads below are unconditional from clamped addresses, with the value
 // selected afterwards: branch-free code keeps the compiler's vmcnt waits exact,
 // so MFMAs start on the first W k-step while later ones are still in flight.
 __device__ __forceinline__ u32x4_t sel(bool keep, u32x4_t v) { return keep ? v : zero_u32x4(); }
+
+// Workgroup barrier for LDS data only: waits for this wave's LDS (and scalar)
+// operations, not for its outstanding global loads, which __syncthreads
+// would wait for too. The memory clobber keeps the compiler from moving
+// memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 template <int TT>
 __global__ __launch_bounds__(kDecThreads) void k_stream_bf16(DecodeArgs a) {
@@ -93,22 +85,33 @@ __global__ __launch_bounds__(kDecThreads) void k_stream_bf16(DecodeArgs a) {
   const uint16_t* __restrict__ W = (const uint16_t*)a.W;
   const bool lora = a.lora_on != 0;
 
-  // ---- 0. segment metadata: the last wave builds the segment table --------
-  // Its loads go first in that wave's queue (branch-free, clamped indices), so
-  // the wait for them does not wait for the x and W loads issued after them.
-  constexpr int kMetaWave = kDecThreads / kWave - 1;
-  const int nseg = lora ? min(seg_count(a.sv), kDecMaxSeg) : 0;
-  int m_st[5] = {0, 0, 0, 0, 0}, m_ad[4] = {-1, -1, -1, -1}, m_r[4] = {0, 0, 0, 0};
-  if (lora && wave == kMetaWave && nseg > 0) {   // wave-uniform branch
-#pragma unroll
-    for (int i = 0; i < 5; ++i) m_st[i] = a.sv.seg_start[min(lane * 4 + i, nseg)];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int s = min(lane * 4 + i, nseg - 1);
-      m_ad[i] = a.sv.seg_adapter[s];
-      m_r[i] = a.sv.seg_rank[s];
-    }
-  }
+  // ---- 0. this item's shrink units -----------------------------------------
+  // A unit is ur = a.unit_rows (4, 8 or 16) consecutive rank rows of one
+  // segment: unit u = s * nq + q holds rows [q ur, (q + 1) ur) of segment s,
+  // nq = ceil(max_rank / ur). Lane l of every wave holds unit tile + l * n_tiles
+  // (at most 64 per item, which the host guarantees). The lane's segment
+  // metadata loads go first in the queue, from clamped indices (without LoRA
+  // they read the pool's zero block), so the waits for them never wait for the
+  // x and W loads issued after them.
+  // The device segment count, when there is one, is read the same way: the
+  // offset vz is zero, but held in a vector register, so the load is a vector
+  // load (ordered with the others) rather than a scalar one, whose wait would
+  // come at once.
+  int vz;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(vz));
+  const int32_t* zi = (const int32_t*)a.pv.zeros;
+  const bool nsd_on = lora && a.sv.n_seg_dev != nullptr;
+  const int nsd = *((nsd_on ? a.sv.n_seg_dev : zi) + vz);
+  const int ur = a.unit_rows;
+  const int nq = (a.pv.max_rank + ur - 1) / ur;
+  const int u_l = tile + lane * a.n_tiles;
+  const int s_l = u_l / nq, j0_l = (u_l - s_l * nq) * ur;   // segment, first rank row
+  const int si = lora ? min(s_l, max(a.sv.n_seg - 1, 0)) : 0;
+  const int m_st0 = *(lora ? a.sv.seg_start + si : zi);
+  const int m_st1 = *(lora ? a.sv.seg_start + si + 1 : zi);
+  const int m_ad = *(lora ? a.sv.seg_adapter + si : zi);
+  const int m_rk = *(lora ? a.sv.seg_rank + si : zi);
+  const float m_sc = *(lora ? a.sv.seg_scale + si : (const float*)zi);
 
   // ---- 1. x chunk -> registers ---------------------------------------------
   // thread's pieces: token t_i = tid/128 + 4 i, 16-byte column tid % 128
@@ -127,81 +130,21 @@ __global__ __launch_bounds__(kDecThreads) void k_stream_bf16(DecodeArgs a) {
 #pragma unroll
   for (int i = 0; i < XCH; ++i) {
     const int t = tid / (kDecMaxKc / 8) + (kDecThreads / (kDecMaxKc / 8)) * i;
-    xr[i] = sel(t < T && xcol_ok, ld16(x + (long long)xrow[i] * d_in + xk));
+    // absent tokens and columns past the chunk read the zero block (an
+    // address select: a select on the loaded value would wait for it here)
+    xr[i] = ld16(t < T && xcol_ok ? x + (long long)xrow[i] * d_in + xk : (const uint16_t*)a.pv.zeros);
   }
-
-  // ---- 3. segment table and shrink-row prefix (one wave, no block barrier) -
-  if (lora && wave == kMetaWave) {
-    // lane owns segments 4*lane .. 4*lane+3; rows to shrink per segment are its
-    // rank capped by the slot size (the slot table is read by k_finish, which
-    // drops emptied slots)
-    int rr[4], tot = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int sg = lane * 4 + i;
-      const int ps = max(m_st[i], 0), pe = min(m_st[i + 1], T);
-      const bool ok = sg < nseg && pe > ps && m_ad[i] >= 0 && m_ad[i] < a.pv.capacity && m_r[i] > 0;
-      rr[i] = ok ? min(m_r[i], a.pv.max_rank) : 0;
-      tot += rr[i];
-      if (sg < nseg) {
-        sm.sad[sg] = ok ? m_ad[i] : -1;
-        sm.sps[sg] = ps;
-        sm.spe[sg] = pe;
-      }
-    }
-    // inclusive wave scan of the lane totals
-    int inc = tot;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const int up = __shfl_up(inc, off, kWave);
-      if (lane >= off) inc += up;
-    }
-    int run = inc - tot;
-    int p0[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int sg = lane * 4 + i;
-      p0[i] = run;
-      if (sg < nseg) sm.pref[sg] = run;
-      run += rr[i];
-    }
-    if (lane == kWave - 1) sm.pref[nseg] = inc;   // total rows (nseg <= 256 = 4 * 64)
-    // Direct lookup tables by scatter, so no lane needs a search later: the
-    // segment and rank row of the item's first kDecRowWin shrink rows, and the
-    // segment of every sorted position (item 0 writes the position table).
-    const int rtot = __shfl(inc, kWave - 1, kWave);
-    const int qb0 = (int)((long long)tile * rtot / a.n_tiles);
-    const int qe0 = min((int)((long long)(tile + 1) * rtot / a.n_tiles), qb0 + kDecRowWin);
-    if (lane < T) sm.posseg[lane] = -1;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int sg = lane * 4 + i;
-      for (int q = max(p0[i], qb0); q < min(p0[i] + rr[i], qe0); ++q) {
-        sm.rseg[q - qb0] = sg;
-        sm.rj[q - qb0] = q - p0[i];
-      }
-      if (sg < nseg)
-        for (int q = max(m_st[i], 0); q < min(m_st[i + 1], T); ++q) sm.posseg[q] = sg;
-    }
-  }
-
-  // ---- 5. x registers -> LDS -----------------------------------------------
-#pragma unroll
-  for (int i = 0; i < XCH; ++i) {
-    const int t = tid / (kDecMaxKc / 8) + (kDecThreads / (kDecMaxKc / 8)) * i;
-    *(u32x4_t*)&sm.xs[t * XP + xcol * 8] = xr[i];
-  }
-  __syncthreads();
 
   // ---- 2. W rows -> MFMA A-operand registers --------------------------------
-  // wave w: row block rb = w % 4, k-half kh = w / 4 of the chunk. The first
-  // kDecWPre k-steps are requested now; the MFMA loop requests one more step
-  // per step it consumes, so the MFMAs run while W streams in instead of
-  // after the wave has finished issuing the whole chunk. W is requested only
-  // once x is in LDS: x's misses would otherwise queue behind the W stream of
-  // every CU. Addresses past the chunk or d_out are clamped into the row:
-  // their products meet zero x columns or land in discarded rows; steps that
-  // belong to the other k-half read zeros. No select on a loaded value.
+  // wave w: row block rb = w % 4, k-half kh = w / 4 of the chunk. Its first
+  // kDecWPre k-steps are requested right behind the x loads, the rest inside
+  // the MFMA loop, kDecWPre steps ahead of the step being multiplied: x's
+  // requests lead every CU's queue, and HBM streams W while x lands (the
+  // barrier below waits for LDS only, not for these loads). Requesting all of
+  // the wave's W up front measured slower: x then lands later. Addresses past the chunk or d_out are clamped
+  // into the row: their products meet zero x columns or land in discarded
+  // rows; steps that belong to the other k-half read zeros. No select on a
+  // loaded value.
   const int rb = wave & 3, kh = wave >> 2;
   const int nrow = tile * kDecRows + rb * 16 + l16;
   const int half_steps = (nks + 1) / 2;
@@ -216,50 +159,52 @@ __global__ __launch_bounds__(kDecThreads) void k_stream_bf16(DecodeArgs a) {
   };
 #pragma unroll
   for (int s = 0; s < kDecWPre; ++s) load_w(s);
+  // nothing below is hoisted between these loads (it would wait for the
+  // metadata before the last of them are issued)
+  __builtin_amdgcn_sched_barrier(0);
 
-  // ---- per-position table for k_finish ------------------------------------
-  // One item resolves every sorted position's segment once (adapter checked
-  // against the pool's slot table, rank, scale), so the finish kernel reads
-  // one entry per token instead of walking the metadata. Its loads are issued
-  // here and only waited for after the W MFMAs.
-  const bool pos_writer = lora && blockIdx.x == 0 && tid < T;
-  int pos_ad = -1, pos_r = 0, pos_s = 0;
-  float pos_sc = 0.f;
-  if (pos_writer) {
-    const int sg = sm.posseg[tid];
-    pos_s = sg >= 0 ? sg : 0;
-    pos_ad = sg >= 0 ? sm.sad[sg] : -1;
-    pos_r = a.pv.rank[pos_ad >= 0 ? pos_ad : 0];   // registered rank; used after the MFMAs
-    pos_sc = a.sv.seg_scale[pos_s];
+  // ---- 3. rows to shrink per unit -------------------------------------------
+  // the segment's rank capped by the slot size (the registered rank is applied
+  // by the position table, which k_finish reads), cut to the unit's rows
+  const int nseg = !lora ? 0 : nsd_on ? min(max(nsd, 0), a.sv.n_seg) : a.sv.n_seg;
+  const bool s_ok = s_l < nseg;
+  const int ps_l = max(m_st0, 0), pe_l = min(m_st1, T);
+  const bool live_l = s_ok && pe_l > ps_l && m_ad >= 0 && m_ad < a.pv.capacity && m_rk > 0;
+  const int rr_l = live_l ? min(m_rk, a.pv.max_rank) : 0;
+  const int rows_l = min(max(rr_l - j0_l, 0), ur);
+  const unsigned long long umask = __ballot(rows_l > 0);   // wave-uniform
+
+  // ---- 4. x registers -> LDS -----------------------------------------------
+#pragma unroll
+  for (int i = 0; i < XCH; ++i) {
+    const int t = tid / (kDecMaxKc / 8) + (kDecThreads / (kDecMaxKc / 8)) * i;
+    *(u32x4_t*)&sm.xs[t * XP + xcol * 8] = xr[i];
   }
+  // registered rank of the lane's adapter, for the position table written by
+  // wave 0 of the chunk-0 items, lanes of a segment's first unit (the others
+  // read the zero block)
+  const bool pos_item = lora && c == 0 && wave == 0;
+  const bool pos_lane = s_l < nseg && j0_l == 0;
+  const int reg_r = *(pos_item && pos_lane && live_l ? a.pv.rank + m_ad : zi);
+  lds_barrier();
 
-  // ---- 4. shrink rows of this item: first two blocks of A rows -------------
-  // (after the barrier: the segment table is in LDS; these loads overlap the
-  // W MFMAs below)
-  const int R = lora ? sm.pref[nseg] : 0;
-  const int q_begin = (int)((long long)tile * R / a.n_tiles);
-  const int q_end = (int)((long long)(tile + 1) * R / a.n_tiles);
+  // ---- 5. shrink units, visited in lane order -------------------------------
+  // The A rows of the first two are requested now, so they stream in under the
+  // W MFMAs. An absent row reads the pool's zero block; k past the chunk reads
+  // a clamped in-row address whose product meets zero x in LDS.
+  auto next_unit = [&](int i) {
+    const unsigned long long rest = i >= kWave - 1 ? 0ull : umask & (~0ull << (i + 1));
+    return rest ? (int)__builtin_ctzll(rest) : kWave;
+  };
   u32x4_t ar[2][kDecASteps];
-  auto load_a = [&](int qb, u32x4_t* dst) {
-    // no select on the loaded value (it would wait for the load right away):
-    // an absent row reads the pool's zero block, and k past the chunk reads a
-    // clamped in-row address whose product meets zero x in LDS
-    const int q = qb + l16;
-    const bool qok = q < q_end;
-    const int qq = qok ? q : q_begin;
-    int s, j;
-    if (qb + 16 <= q_begin + kDecRowWin) {   // uniform: rows in the lookup window
-      // (the entry is unset when the item has no rows: qok is false then)
-      s = qok ? min(max(sm.rseg[qq - q_begin], 0), kDecMaxSeg - 1) : 0;
-      j = sm.rj[qq - q_begin];
-    } else {
-      s = seg_of_row(sm.pref, nseg, qq);
-      j = qq - sm.pref[s];
-    }
-    const int ad = qok ? sm.sad[s] : -1;
-    const bool rok = qok && nseg > 0 && ad >= 0;
+  auto load_a = [&](int i, u32x4_t* dst) {
+    const int ii = i < kWave ? i : 0;
+    const int rows = i < kWave ? __builtin_amdgcn_readlane(rows_l, ii) : 0;
+    const int j0 = __builtin_amdgcn_readlane(j0_l, ii);
+    const int ad = __builtin_amdgcn_readlane(m_ad, ii);
+    const bool rok = l16 < rows;
     const uint16_t* arow = rok ? (const uint16_t*)a.pv.base + (long long)ad * a.pv.slot_elems +
-                                     (long long)j * d_in + k0
+                                     (long long)(j0 + l16) * d_in + k0
                                : (const uint16_t*)a.pv.zeros;
     const int klim = rok ? kc - 8 : kZeroBlockElems - 8;
 #pragma unroll
@@ -268,52 +213,12 @@ __global__ __launch_bounds__(kDecThreads) void k_stream_bf16(DecodeArgs a) {
       dst[st] = ld16(arow + min(k, klim));
     }
   };
-  // issued unconditionally (rows past q_end read zeros): a branch here would
+  int bi = umask ? (int)__builtin_ctzll(umask) : kWave;   // unit in ar[0]
+  int ni = next_unit(bi);                                 // unit in ar[1]
+  // issued unconditionally (absent units read zeros): a branch here would
   // make the compiler's waits for the W loads below conservative
-  load_a(q_begin, ar[0]);
-  load_a(q_begin + 16, ar[1]);
-
-  // output rows of shrink block qb held by this lane (qb + 4*(lane/16) + v):
-  // segment, rank row, token range, and the token blocks the block covers.
-  // Computed for the first block here, while the W loads are in flight.
-  struct RowInfo { int os[4], oj[4], o0[4], o1[4], tb_lo, tb_hi; };
-  auto row_info = [&](int qb) {
-    RowInfo ri;
-    int tlo = T, thi = 0;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int q = qb + 4 * (lane / 16) + v;
-      ri.os[v] = -1;
-      ri.oj[v] = 0;
-      ri.o0[v] = 0;
-      ri.o1[v] = 0;
-      if (q < q_end) {
-        int sg, jj;
-        if (qb + 16 <= q_begin + kDecRowWin) {   // uniform: rows in the lookup window
-          sg = sm.rseg[q - q_begin];
-          jj = sm.rj[q - q_begin];
-        } else {
-          sg = seg_of_row(sm.pref, nseg, q);
-          jj = q - sm.pref[sg];
-        }
-        ri.os[v] = sg;
-        ri.oj[v] = jj;
-        ri.o0[v] = sm.sps[sg];
-        ri.o1[v] = sm.spe[sg];
-        tlo = min(tlo, ri.o0[v]);
-        thi = max(thi, ri.o1[v]);
-      }
-    }
-    // wave-uniform range: lanes 0, 16, 32 and 48 hold the block's 16 rows
-    tlo = min(tlo, __shfl_xor(tlo, 16, kWave));
-    tlo = min(tlo, __shfl_xor(tlo, 32, kWave));
-    thi = max(thi, __shfl_xor(thi, 16, kWave));
-    thi = max(thi, __shfl_xor(thi, 32, kWave));
-    ri.tb_lo = tlo / 16;
-    ri.tb_hi = thi > tlo ? (thi - 1) / 16 : ri.tb_lo - 1;
-    return ri;
-  };
-  RowInfo ri0 = row_info(q_begin);
+  load_a(bi, ar[0]);
+  load_a(ni, ar[1]);
 
   // ---- 6. base MFMAs --------------------------------------------------------
   f32x4_t acc[NTB];
@@ -349,21 +254,30 @@ __global__ __launch_bounds__(kDecThreads) void k_stream_bf16(DecodeArgs a) {
       *(f32x4_t*)(a.ypart + part_off(c, tile, rb, tb, a.n_tiles, NTB) + lane * 4) = o;
     }
   }
-  if (pos_writer) {
-    const int r = pos_ad >= 0 ? min(sm.pref[pos_s + 1] - sm.pref[pos_s], pos_r) : 0;
-    const int ad = r > 0 ? pos_ad : -1;
-    a.pos[tid] = make_int4(ad, ad >= 0 ? r : 0, __float_as_int(ad >= 0 ? pos_sc : 0.f), 0);
-  }
-  if (q_begin >= q_end) return;   // uniform: no shrink rows in this item
 
-  // ---- 7. shrink row blocks -------------------------------------------------
-  // Each wave writes its own k-slice of the block straight to
+  // ---- 7. position table for k_finish --------------------------------------
+  // Every sorted position's entry {adapter or -1, rank, scale bits}: the rank
+  // is the segment's capped by the registered one, so a lying rank never reads
+  // past the registered adapter and an emptied slot drops out. The lane of a
+  // segment's first unit writes the segment's positions.
+  if (pos_item) {   // uniform
+    const int r = live_l ? min(rr_l, reg_r) : 0;
+    const int ad = r > 0 ? m_ad : -1;
+    const int4 e = make_int4(ad, ad >= 0 ? r : 0, __float_as_int(ad >= 0 ? m_sc : 0.f), 0);
+    if (pos_lane)
+      for (int t = ps_l; t < pe_l; ++t) a.pos[t] = e;
+  }
+
+  // ---- 8. shrink units -------------------------------------------------------
+  // Each wave writes its own k-slice of the unit straight to
   // v_part[c][wave][t][j] (k_finish sums the 8 * n_chunks slices in a fixed
   // order): no barrier after the W MFMAs.
-  int buf = 0;
-  for (int qb = q_begin; qb < q_end; qb += 16, buf ^= 1) {
-    const RowInfo ri = qb == q_begin ? ri0 : row_info(qb);
-    const int tb_lo = ri.tb_lo, tb_hi = ri.tb_hi;
+  float* vp = a.v_part + ((long long)c * kDecWaves + wave) * T * a.r_ws;
+  auto shrink_unit = [&](u32x4_t* cur) {
+    const int rows = __builtin_amdgcn_readlane(rows_l, bi);
+    const int j0 = __builtin_amdgcn_readlane(j0_l, bi);
+    const int ps = __builtin_amdgcn_readlane(ps_l, bi), pe = __builtin_amdgcn_readlane(pe_l, bi);
+    const int tb_lo = ps / 16, tb_hi = (pe - 1) / 16;
     f32x4_t vacc[NTB];
 #pragma unroll
     for (int tb = 0; tb < NTB; ++tb) vacc[tb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -374,19 +288,29 @@ __global__ __launch_bounds__(kDecThreads) void k_stream_bf16(DecodeArgs a) {
       for (int tb = 0; tb < NTB; ++tb) {
         if (tb < tb_lo || tb > tb_hi) continue;
         const u32x4_t xo = *(const u32x4_t*)&sm.xs[(tb * 16 + l16) * XP + ks * 32 + kq];
-        vacc[tb] = mfma16d(ar[buf][st], xo, vacc[tb]);
+        vacc[tb] = mfma16d(cur[st], xo, vacc[tb]);
       }
     }
-    if (qb + 32 < q_end) load_a(qb + 32, ar[buf]);   // refill this buffer two blocks ahead
-    float* vp = a.v_part + ((long long)c * kDecWaves + wave) * T * a.r_ws;
+    // refill this buffer with the unit after next
+    const int n2 = next_unit(ni);
+    if (n2 < kWave) load_a(n2, cur);
 #pragma unroll
     for (int tb = 0; tb < NTB; ++tb) {
       if (tb < tb_lo || tb > tb_hi) continue;
       const int t = tb * 16 + l16;
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
-        if (ri.os[v] >= 0 && t >= ri.o0[v] && t < ri.o1[v]) vp[(long long)t * a.r_ws + ri.oj[v]] = vacc[tb][v];
+      for (int v = 0; v < 4; ++v) {
+        const int jr = 4 * (lane / 16) + v;
+        if (jr < rows && t >= ps && t < pe) vp[(long long)t * a.r_ws + j0 + jr] = vacc[tb][v];
+      }
     }
+    bi = ni;
+    ni = n2;
+  };
+  while (bi < kWave) {   // uniform
+    shrink_unit(ar[0]);
+    if (bi >= kWave) break;
+    shrink_unit(ar[1]);
   }
 }
 
@@ -424,20 +348,6 @@ __global__ __launch_bounds__(256) void k_finish_bf16(DecodeArgs a) {
 #pragma unroll
   for (int u = 0; u < kFinUnroll; ++u) p[u] = *(const f32x4_t*)(pbase + min(u, a.n_chunks - 1) * cstride);
 
-  // B rows of the lane's adapter (first 16 rank columns), as soon as the
-  // position entry is in
-  const int ad = pe.x, r = min(pe.y, a.pv.max_rank);
-  const bool live = lora && ad >= 0 && ad < a.pv.capacity && r > 0 && t < T;
-  const uint16_t* Bb = (const uint16_t*)(live ? a.pv.base : a.pv.zeros) +
-                       (live ? (long long)ad * a.pv.slot_elems + a.pv.b_offset : 0);
-  const int bld = live ? round_up8(r) : 0;
-  u32x4_t b8[kPre][4];
-#pragma unroll
-  for (int g = 0; g < kPre; ++g)
-#pragma unroll
-    for (int v = 0; v < 4; ++v)
-      b8[g][v] = ld16(Bb + (live ? (long long)min(n + v, d_out - 1) * bld + min(8 * g, bld - 8) : 0));
-
   // v of the 16 tokens: sum of the stream kernel's slices [c][w]. A 16-byte
   // quad of one token is element e; G groups of threads each sum every G-th
   // slice of an element, then the groups are added in group order. The first
@@ -452,11 +362,32 @@ __global__ __launch_bounds__(256) void k_finish_bf16(DecodeArgs a) {
     return a.v_part + (long long)min(tb * 16 + e / nq, T - 1) * a.r_ws + 4 * (e % nq);
   };
   f32x4_t vq[kFinUnroll];
-  if (lora) {
+  {
+    // without LoRA every lane reads the pool's zero block (an address select
+    // keeps the loads unconditional)
     const float* vp = vptr(0);
 #pragma unroll
-    for (int u = 0; u < kFinUnroll; ++u) vq[u] = *(const f32x4_t*)(vp + min(tid % G + u * G, nsl - 1) * vstride);
+    for (int u = 0; u < kFinUnroll; ++u)
+      vq[u] = *(const f32x4_t*)(lora ? vp + min(tid % G + u * G, nsl - 1) * vstride : (const float*)a.pv.zeros);
   }
+  // the slice loads stay ahead of the B loads, which wait for the position
+  // entry: the v sums below then wait for them alone
+  __builtin_amdgcn_sched_barrier(0);
+
+
+  // B rows of the lane's adapter (first 16 rank columns), as soon as the
+  // position entry is in
+  const int ad = pe.x, r = min(pe.y, a.pv.max_rank);
+  const bool live = lora && ad >= 0 && ad < a.pv.capacity && r > 0 && t < T;
+  const uint16_t* Bb = (const uint16_t*)(live ? a.pv.base : a.pv.zeros) +
+                       (live ? (long long)ad * a.pv.slot_elems + a.pv.b_offset : 0);
+  const int bld = live ? round_up8(r) : 0;
+  u32x4_t b8[kPre][4];
+#pragma unroll
+  for (int g = 0; g < kPre; ++g)
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      b8[g][v] = ld16(Bb + (live ? (long long)min(n + v, d_out - 1) * bld + min(8 * g, bld - 8) : 0));
 
   // chunk partials summed in chunk order
   f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -501,7 +432,7 @@ __global__ __launch_bounds__(256) void k_finish_bf16(DecodeArgs a) {
           }
       }
       vgrp[g][tid / G] = sum;
-      __syncthreads();
+      lds_barrier();   // LDS only: the B loads stay in flight
       if (tid < 256 / G && e0 + tid < E) {
         f32x4_t tot = vgrp[0][tid];
         for (int gg = 1; gg < G; ++gg) {
@@ -513,7 +444,7 @@ __global__ __launch_bounds__(256) void k_finish_bf16(DecodeArgs a) {
         const int ee = e0 + tid;
         *(f32x4_t*)&vs[ee / nq][4 * (ee % nq)] = tot;
       }
-      __syncthreads();
+      lds_barrier();
     }
     if (live) {
       const float* vv = vs[lane % 16];
@@ -561,8 +492,20 @@ __global__ __launch_bounds__(256) void k_finish_bf16(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-bool decode_supported(int T, int n_seg_bound) {
-  return T >= 1 && T <= 64 && n_seg_bound <= kDecMaxSeg;
+bool decode_supported(int T, int n_seg_bound, int d_out, int max_rank) {
+  // k_stream gives each item at most one wave's worth (64) of shrink units
+  const long long n_tiles = (d_out + kDecRows - 1) / kDecRows;
+  const long long units16 = (long long)n_seg_bound * ((max_rank + 15) / 16);
+  return T >= 1 && T <= 64 && n_seg_bound <= kDecMaxSeg && units16 <= kWave * n_tiles;
+}
+
+// Rows per shrink unit: the smallest of 4, 8, 16 whose units (one per segment
+// and row group) fit one per item of a chunk, so the A rows spread over as
+// many items as possible; 16 when none does.
+int decode_unit_rows(int n_seg_bound, int max_rank, int n_tiles) {
+  for (int ur = 4; ur < 16; ur *= 2)
+    if ((long long)n_seg_bound * ((max_rank + ur - 1) / ur) <= n_tiles) return ur;
+  return 16;
 }
 
 // d_in chunk: a multiple of 64 (at most the LDS x chunk), small enough that

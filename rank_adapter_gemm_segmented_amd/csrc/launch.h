@@ -42,12 +42,13 @@ struct DecodeArgs {
   SegView sv;
   PoolView pv;
   float* ypart;    // workspace: partial tiles [n_chunks][n_tiles][4][T/16 blocks][256]
-  float* v_part;   // workspace: shrink partials [n_chunks][T][r_ws]
+  float* v_part;   // workspace: shrink partials [n_chunks][8 waves][T][r_ws]
   int4* pos;       // workspace: per sorted position {adapter or -1, rank, scale bits, 0} [T]
   int r_ws;
   int n_tiles;     // ceil(d_out / 64)
   int kc;          // d_in chunk width (multiple of 64)
   int n_chunks;    // ceil(d_in / kc)
+  int unit_rows;   // rank rows per shrink unit (4, 8 or 16)
 };
 
 // metadata kernels (kernels_meta.hip)
@@ -70,7 +71,8 @@ int choose_shrink_split_bf16(int d_in, int seg_grid);
 int shrink_items_bound(int T, int n_seg_bound);
 
 // decode path (kernels_decode.hip)
-bool decode_supported(int T, int n_seg_bound);
+bool decode_supported(int T, int n_seg_bound, int d_out, int max_rank);
+int decode_unit_rows(int n_seg_bound, int max_rank, int n_tiles);
 void decode_plan(int d_in, int d_out, int* n_tiles, int* kc, int* n_chunks);
 void launch_decode_bf16(const DecodeArgs& a, hipStream_t st);
 

@@ -112,6 +112,12 @@ def _edge_cases():
     cases.append((9, "f32", 256, 256, np.random.default_rng(9).integers(-1, 4, size=33).tolist(),
                   {0: 8, 1: 8, 2: 4, 3: 1}, None, False))
     cases.append((10, "bf16", 64, 64, [0, 1], {0: 256, 1: 100}, None, True))          # large ranks
+    # small-T path with device-built segments (unsorted ids)
+    cases.append((11, "bf16", 320, 200, np.random.default_rng(11).integers(-1, 10, size=50).tolist(),
+                  {a: [8, 16, 32, 64, 24][a % 5] for a in range(10)}, None, False))
+    # 64 one-token segments on a single 64-row tile: one shrink segment per lane
+    cases.append((12, "bf16", 192, 64, list(range(64)), {a: [8, 16, 4, 12][a % 4] for a in range(64)},
+                  None, True))
     return cases
 
 
