@@ -256,31 +256,79 @@ __global__ __launch_bounds__(256) void k_vfinal(LinearArgs a) {
 // ---------------------------------------------------------------------------
 // GEMM + fused expand
 // ---------------------------------------------------------------------------
-constexpr int kGKB = 64;            // k per pipeline stage
 constexpr int kBatch = 8;           // independent loads per thread in bulk LDS copies
 constexpr int kEpiRing = 16;        // B operand loads in flight per lane in the expand epilogue
 constexpr int kEpiMaxUnits = 128;   // work units one wave lists per rank chunk (more: further passes)
-constexpr int kGPitch = kGKB + 8;   // LDS row pitch in bf16 (144 bytes)
 
-template <int BR, int BT, int WR, int WT, int PD>
+// LDS address (byte offset in the workgroup's LDS) of a pointer into __shared__ memory
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// Direct global -> LDS load (gfx950 LDS DMA): the wave's 64 lanes each fetch
+// 16 bytes from their own global address and the data lands in LDS, lane l at
+// byte m0 + 16 l, without passing through registers. Issued as inline
+// assembly so that the compiler, which would otherwise wait for every
+// outstanding DMA before any LDS read, leaves the waits to the stage ring
+// below. One wait state separates the M0 write from its use.
+__device__ __forceinline__ void dma16(const void* g, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0)
+               : "memory", "m0");
+}
+
+// Wait until at most N of this wave's vector memory operations are in flight,
+// then a workgroup barrier (LDS and scalar counters drained too; nothing else).
+template <int N>
+__device__ __forceinline__ void vm_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// KB: k per stage (32 or 64). A stage holds the tile's BR W rows then its BT
+// positions. DMA: the stages reach LDS by direct loads, in a ring of NB LDS
+// slots (NB - 1 in flight while one is multiplied); rows are 2 KB bytes,
+// unpadded, and 16-byte chunk c of row r sits in slot c ^ swz(r) of the row,
+// so the rows read together by one fragment load fall in distinct LDS banks.
+// Otherwise the stages pass through registers (NB - 1 in flight there) into
+// two LDS slots whose rows are padded to 2 KB + 16 bytes instead.
+template <int BR, int BT, int WR, int WT, int NB, int KB, bool DMA>
 struct GCfg {
   static constexpr int NWR = BR / WR, NWT = BT / WT;
   static constexpr int NW = NWR * NWT;
   static constexpr int NT = NW * kWave;
   static constexpr int MR = WR / 32, MT = WT / 32;        // 32x32 blocks per wave
-  static constexpr int ROWS = BR + BT;                     // LDS rows per stage
-  static constexpr int CPT = ROWS * (kGKB / 8) / NT;       // 16-byte pieces per thread per stage
-  static constexpr int STAGE = ROWS * kGPitch;             // bf16 per stage
-  static constexpr int MAIN_BYTES = 2 * STAGE * 2;
+  static constexpr int ROWS = BR + BT;                     // rows per stage
+  static constexpr int RB = DMA ? 2 * KB : 2 * KB + 16;    // bytes per LDS row
+  static constexpr int STAGE_B = ROWS * RB;                // bytes per stage
+  static constexpr int DPW = ROWS * 2 * KB / 1024 / NW;    // 1 KB loads per wave per stage
+  static constexpr int MAIN_BYTES = (DMA ? NB : 2) * STAGE_B;
   // small row tiles get extra LDS so the epilogue stages many segment runs at once
   static constexpr int LDS_BYTES = MAIN_BYTES > 96 * 1024 ? MAIN_BYTES : 96 * 1024;
-  static_assert((ROWS * (kGKB / 8)) % NT == 0, "stage pieces must divide the threads");
+  static_assert(KB == 32 || KB == 64, "stage depth");
+  static_assert((ROWS * 2 * KB) % (1024 * NW) == 0, "a stage splits into whole loads per wave");
+  static_assert(NB >= 2 && (NB - 2) * DPW <= 63, "vmcnt range");
 };
 
-template <int BR, int BT, int WR, int WT, int PD>
-__global__ __launch_bounds__((BR / WR) * (BT / WT) * kWave) void k_gemm2(LinearArgs a) {
-  using C = GCfg<BR, BT, WR, WT, PD>;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_BYTES / 2];
+template <int KB>
+__device__ __forceinline__ int gswz(int r) { return KB == 64 ? (r & 7) : ((r >> 1) & 3); }
+
+// Scheduling hint for one k-step: the R fragment reads of the next k-step
+// spread over the M MFMAs of this one (one read, then its share of MFMAs).
+template <int R, int M, int J = 0>
+__device__ __forceinline__ void sched_reads_over_mfma() {
+  if constexpr (J < R) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                          // DS read
+    __builtin_amdgcn_sched_group_barrier(0x008, M * (J + 1) / R - M * J / R, 0);  // MFMA
+    sched_reads_over_mfma<R, M, J + 1>();
+  }
+}
+
+// One workgroup per CU (the LDS stages take most of it): the register
+// allocator may then use the whole register file (waves_per_eu 1).
+template <int BR, int BT, int WR, int WT, int NB, int KB, bool DMA>
+__global__ __launch_bounds__((BR / WR) * (BT / WT) * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_gemm2(LinearArgs a) {
+  using C = GCfg<BR, BT, WR, WT, NB, KB, DMA>;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[C::LDS_BYTES / 2];
   __shared__ int4 pinfo[BT];
 
   // wave index made scalar: every per-wave quantity below is then uniform
@@ -295,24 +343,47 @@ __global__ __launch_bounds__((BR / WR) * (BT / WT) * kWave) void k_gemm2(LinearA
   const uint16_t* __restrict__ W = (const uint16_t*)a.W;
   const uint16_t* zeros = (const uint16_t*)a.pv.zeros;
 
-  // loader: piece q = tid + NT*i -> stage row R = q / 8 (W rows first, then
-  // positions), 16-byte column q % 8
-  const uint16_t* src[C::CPT];
-  int dst[C::CPT];
+  // loader: load i of wave w fills the stage's 1 KB chunk J = i NW + w; lane
+  // l writes its byte J 1024 + 16 l, i.e. stage row r, slot l % (KB/8), and so
+  // fetches chunk (slot ^ swz(r)) of that row (W rows first, then the gathered
+  // rows of the tile's positions)
+  // (register path: piece q = tid + NT i is row q / (KB/8), chunk q % (KB/8),
+  // stored unswizzled at its padded place)
+  const uint16_t* src[C::DPW];
+  int scol[C::DPW];
 #pragma unroll
-  for (int i = 0; i < C::CPT; ++i) {
+  for (int i = 0; i < C::DPW; ++i) {
+    const int J = i * C::NW + wave;
     const int q = tid + C::NT * i;
-    const int R = q / 8, cc = q % 8;
-    dst[i] = R * kGPitch + cc * 8;
-    if (R < BR) {
-      src[i] = W + (long long)min(r0 + R, d_out - 1) * d_in + cc * 8;
+    const int r = DMA ? J * (1024 / (2 * KB)) + lane / (KB / 8) : q / (KB / 8);
+    const int c = DMA ? (lane % (KB / 8)) ^ gswz<KB>(r) : q % (KB / 8);
+    scol[i] = c * 8;
+    if (r < BR) {
+      src[i] = W + (long long)min(r0 + r, d_out - 1) * d_in + c * 8;
     } else {
-      const int p = min(t0 + R - BR, T - 1);
+      const int p = min(t0 + r - BR, T - 1);
       int row = a.sv.token_index ? a.sv.token_index[p] : p;
       row = min(max(row, 0), T - 1);
-      src[i] = x + (long long)row * d_in + cc * 8;
+      src[i] = x + (long long)row * d_in + c * 8;
     }
   }
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
+  // stage st -> ring slot st % NB; stages past d_in (and the k tail) read the
+  // zero block, so every stage issues the same DMA count and the ring's vmcnt
+  // waits stay exact
+  auto issue = [&](int st) {
+    const int k0 = st * KB;
+    const uint32_t sb = lds0 + (uint32_t)(st % NB) * C::STAGE_B + (uint32_t)wave * 1024;
+    if (k0 + KB <= d_in) {   // uniform: whole stage inside d_in
+#pragma unroll
+      for (int i = 0; i < C::DPW; ++i) dma16(src[i] + k0, sb + (uint32_t)i * C::NW * 1024);
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::DPW; ++i)
+        dma16(k0 + scol[i] < d_in ? src[i] + k0 : zeros, sb + (uint32_t)i * C::NW * 1024);
+    }
+  };
+
   f32x16_t acc[C::MR][C::MT];
 #pragma unroll
   for (int m = 0; m < C::MR; ++m)
@@ -321,69 +392,115 @@ __global__ __launch_bounds__((BR / WR) * (BT / WT) * kWave) void k_gemm2(LinearA
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[m][n][v] = 0.f;
 
-  // PD stages of global loads in flight in a register ring; LDS is double-buffered
-  u32x4_t stg[PD][C::CPT];
-  auto load = [&](int st, u32x4_t* dstr) {
-    const int k0 = st * kGKB;
+  // fragment reads: row R (a multiple of 32 plus l32), chunk kk 2 + kh / 8
+  int fcol[KB / 16];
 #pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int k = k0 + (tid + C::NT * i) % 8 * 8;
-      // past d_in: read the zero block (address select keeps the load branch-free)
-      dstr[i] = ld16(k < d_in ? src[i] + k0 : zeros);
-    }
-  };
-  auto store = [&](int buf, const u32x4_t* srcr) {
-#pragma unroll
-    for (int i = 0; i < C::CPT; ++i) *(u32x4_t*)&lds[buf * C::STAGE + dst[i]] = srcr[i];
-  };
-  auto compute = [&](int buf) {
-    const uint16_t* Ls = lds + buf * C::STAGE;
-#pragma unroll
-    for (int kk = 0; kk < kGKB / 16; ++kk) {
-      u32x4_t af[C::MR], bf[C::MT];
+  for (int kk = 0; kk < KB / 16; ++kk)
+    fcol[kk] = ((DMA ? (kk * 2 + kh / 8) ^ gswz<KB>(l32) : kk * 2 + kh / 8) * 16);
+  // the fragments of k-step kk + 1 are read while k-step kk is multiplied
+  auto compute = [&](int slot) {
+    const char* Ls = (const char*)lds + slot * C::STAGE_B;
+    u32x4_t af[2][C::MR], bf[2][C::MT];
+    auto frag = [&](int kk, u32x4_t* fa, u32x4_t* fb) {
 #pragma unroll
       for (int m = 0; m < C::MR; ++m)
-        af[m] = *(const u32x4_t*)&Ls[(wr * WR + m * 32 + l32) * kGPitch + kk * 16 + kh];
+        fa[m] = *(const u32x4_t*)(Ls + (wr * WR + m * 32 + l32) * C::RB + fcol[kk]);
 #pragma unroll
       for (int n = 0; n < C::MT; ++n)
-        bf[n] = *(const u32x4_t*)&Ls[(BR + wt * WT + n * 32 + l32) * kGPitch + kk * 16 + kh];
+        fb[n] = *(const u32x4_t*)(Ls + (BR + wt * WT + n * 32 + l32) * C::RB + fcol[kk]);
+    };
+    if constexpr (C::MR * C::MT >= 16) {
+      // 128x128 per wave: its 16 MFMAs per k-step cover the LDS latency of the
+      // step's own reads; one fragment set leaves registers for the epilogue
+#pragma unroll
+      for (int kk = 0; kk < KB / 16; ++kk) {
+        frag(kk, af[0], bf[0]);
+#pragma unroll
+        for (int m = 0; m < C::MR; ++m)
+#pragma unroll
+          for (int n = 0; n < C::MT; ++n) acc[m][n] = mfma32g(af[0][m], bf[0][n], acc[m][n]);
+      }
+      return;
+    }
+    frag(0, af[0], bf[0]);
+#pragma unroll
+    for (int kk = 0; kk < KB / 16; ++kk) {
+      if (kk + 1 < KB / 16) frag(kk + 1, af[(kk + 1) & 1], bf[(kk + 1) & 1]);
 #pragma unroll
       for (int m = 0; m < C::MR; ++m)
 #pragma unroll
-        for (int n = 0; n < C::MT; ++n) acc[m][n] = mfma32g(af[m], bf[n], acc[m][n]);
+        for (int n = 0; n < C::MT; ++n) acc[m][n] = mfma32g(af[kk & 1][m], bf[kk & 1][n], acc[m][n]);
     }
+    __builtin_amdgcn_sched_group_barrier(0x100, C::MR + C::MT, 0);
+#pragma unroll
+    for (int kk = 0; kk + 1 < KB / 16; ++kk) sched_reads_over_mfma<C::MR + C::MT, C::MR * C::MT>();
+    __builtin_amdgcn_sched_group_barrier(0x008, C::MR * C::MT, 0);
   };
 
-  // Stage count padded to a multiple of PD: stages past d_in read the zero
-  // block and add nothing. Every load and store inside the loop is
-  // unconditional, so the compiler's vmcnt waits stay exact (a conditional load
-  // would make them drain the whole prefetch ring at each merge point).
-  const int nst = (d_in + kGKB - 1) / kGKB;
-  const int nst_pad = (nst + PD - 1) / PD * PD;
-  // stage k lives in ring slot k % PD
-  load(0, stg[0]);
-  store(0, stg[0]);
+  const int nst = (d_in + KB - 1) / KB;
+  if constexpr (DMA) {
+    // Ring: before stage st is multiplied, this wave's DMAs of stage st have
+    // landed (those of the NB - 2 later stages may still be in flight) and,
+    // past the barrier, so have every wave's; every wave is also done with
+    // stage st - 1, whose slot then takes stage st + NB - 1.
 #pragma unroll
-  for (int k = 1; k <= PD; ++k) load(k, stg[k % PD]);
-  __syncthreads();
-  for (int st0 = 0; st0 < nst_pad - PD; st0 += PD) {
-#pragma unroll
-    for (int u = 0; u < PD; ++u) {
-      const int st = st0 + u;
-      compute(st & 1);
-      store((st + 1) & 1, stg[(u + 1) % PD]);
-      load(st + 1 + PD, stg[(u + 1) % PD]);
-      __syncthreads();
+    for (int st = 0; st < NB - 1; ++st) issue(st);
+    for (int st = 0; st < nst; ++st) {
+      vm_barrier<(NB - 2) * C::DPW>();
+      issue(st + NB - 1);
+      compute(st % NB);
     }
-  }
-  {  // last PD stages: nothing further to prefetch
-    const int st0 = nst_pad - PD;
+    // the ring's last DMAs (zero stages) land before the LDS is reused
+    vm_barrier<0>();
+  } else {
+    // PD stages of global loads in flight in a register ring (stage k in ring
+    // slot k % PD), two LDS slots. The stage count is padded to a multiple of
+    // PD: stages past d_in read the zero block and add nothing. Every load and
+    // store inside the loop is unconditional, so the compiler's vmcnt waits
+    // stay exact (a conditional load would make them drain the ring).
+    constexpr int PD = NB - 1;
+    u32x4_t stg[PD][C::DPW];
+    auto load = [&](int st, u32x4_t* r) {
+      const int k0 = st * KB;
 #pragma unroll
-    for (int u = 0; u < PD; ++u) {
-      const int st = st0 + u;
-      compute(st & 1);
-      if (u + 1 < PD) store((st + 1) & 1, stg[(u + 1) % PD]);
-      __syncthreads();
+      for (int i = 0; i < C::DPW; ++i) r[i] = ld16(k0 + scol[i] < d_in ? src[i] + k0 : zeros);
+    };
+    int sdst[C::DPW];
+#pragma unroll
+    for (int i = 0; i < C::DPW; ++i) {
+      const int q = tid + C::NT * i;
+      sdst[i] = q / (KB / 8) * C::RB + scol[i] * 2;
+    }
+    auto store = [&](int slot, const u32x4_t* r) {
+      char* Ls = (char*)lds + slot * C::STAGE_B;
+#pragma unroll
+      for (int i = 0; i < C::DPW; ++i) *(u32x4_t*)(Ls + sdst[i]) = r[i];
+    };
+    const int nst_pad = (nst + PD - 1) / PD * PD;
+    load(0, stg[0]);
+    store(0, stg[0]);
+#pragma unroll
+    for (int k = 1; k <= PD; ++k) load(k, stg[k % PD]);
+    __syncthreads();
+    for (int st0 = 0; st0 < nst_pad - PD; st0 += PD) {
+#pragma unroll
+      for (int u = 0; u < PD; ++u) {
+        const int st = st0 + u;
+        compute(st & 1);
+        store((st + 1) & 1, stg[(u + 1) % PD]);
+        load(st + 1 + PD, stg[(u + 1) % PD]);
+        __syncthreads();
+      }
+    }
+    {  // last PD stages: nothing further to prefetch
+      const int st0 = nst_pad - PD;
+#pragma unroll
+      for (int u = 0; u < PD; ++u) {
+        const int st = st0 + u;
+        compute(st & 1);
+        if (u + 1 < PD) store((st + 1) & 1, stg[(u + 1) % PD]);
+        __syncthreads();
+      }
     }
   }
 
@@ -626,11 +743,11 @@ int shrink_items_bound(int T, int n_seg_bound) {
   return (n_seg_bound < kShrMaxSeg ? n_seg_bound : kShrMaxSeg) + (T + 63) / 64;
 }
 
-template <int BR, int BT, int WR, int WT, int PD>
+template <int BR, int BT, int WR, int WT, int NB, int KB, bool DMA>
 static void launch_g(const LinearArgs& a, hipStream_t st) {
   const int n_rt = (a.d_out + BR - 1) / BR, n_tt = (a.T + BT - 1) / BT;
-  hipLaunchKernelGGL((k_gemm2<BR, BT, WR, WT, PD>), dim3(n_rt * n_tt),
-                     dim3(GCfg<BR, BT, WR, WT, PD>::NT), 0, st, a);
+  hipLaunchKernelGGL((k_gemm2<BR, BT, WR, WT, NB, KB, DMA>), dim3(n_rt * n_tt),
+                     dim3(GCfg<BR, BT, WR, WT, NB, KB, DMA>::NT), 0, st, a);
 }
 
 // Tile choice: large batches take 256x256 tiles (MFMA-bound, ~30 B/clk of L2
@@ -661,10 +778,10 @@ void launch_linear_bf16(const LinearArgs& a, hipStream_t st) {
     return (long long)((a.d_out + br - 1) / br) * ((a.T + bt - 1) / bt);
   };
   constexpr long long kFill = 192;   // tiles that keep most of the 256 CUs busy
-  if (a.T > 128 && tiles(256, 256) >= kFill) launch_g<256, 256, 128, 128, 1>(a, st);
-  else if (a.T > 128 && tiles(128, 256) >= kFill) launch_g<128, 256, 64, 128, 2>(a, st);
-  else if (a.T > 128 && tiles(64, 256) >= kFill) launch_g<64, 256, 64, 64, 3>(a, st);
-  else launch_g<64, 128, 32, 64, 4>(a, st);
+  if (a.T > 128 && tiles(256, 256) >= kFill) launch_g<256, 256, 128, 128, 2, 64, false>(a, st);
+  else if (a.T > 128 && tiles(128, 256) >= kFill) launch_g<128, 256, 64, 128, 2, 64, true>(a, st);
+  else if (a.T > 128 && tiles(64, 256) >= kFill) launch_g<64, 256, 64, 64, 3, 64, true>(a, st);
+  else launch_g<64, 128, 32, 64, 4, 64, true>(a, st);
 }
 
 }  // namespace mlora
