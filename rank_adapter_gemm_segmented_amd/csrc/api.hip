@@ -152,7 +152,11 @@ int run_linear(const void* x, const void* W, mlora_pool_s* pool, const SegView& 
       launch_decode_bf16(d, stream);
       return check_launch();
     }
-    a.ks = choose_shrink_split_bf16(pool->d_in, shrink_items_bound(T, a.seg_grid));
+    // short low-rank segments (a verify batch): one d_in chunk, so the shrink
+    // writes the final scaled v and no finalize launch follows (measured
+    // faster there; longer or higher-rank segments gain from the split)
+    const bool one_chunk = lora_on && T <= 16 * a.seg_grid && pool->max_rank <= 16;
+    a.ks = one_chunk ? 1 : choose_shrink_split_bf16(pool->d_in, shrink_items_bound(T, a.seg_grid));
     launch_linear_bf16(a, stream);
   } else {
     a.ks = 1;

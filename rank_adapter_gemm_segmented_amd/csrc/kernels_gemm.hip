@@ -126,11 +126,20 @@ __global__ __launch_bounds__(256) void k_shrink2(LinearArgs a) {
   const int ra = adok ? min(max(rk0, 0), a.pv.max_rank) : 0;
   const int reg_rank = a.pv.rank[adok ? ad0 : 0];
   const float scl = sv.seg_scale[s];
+  // rank the expand applies: the segment's, capped by the registered one
+  const int r_eff = adok && reg_rank > 0 && ra > 0 ? min(ra, reg_rank) : 0;
+  // With one d_in chunk (ks == 1) the sum is final: this kernel writes
+  // v_fin = scale * v itself (zero past r_eff, up to the row pitch) and no
+  // finalize launch follows.
+  const bool fused = a.ks == 1;
   auto write_pos = [&]() {
     if (c != 0) return;
-    const int r = adok && reg_rank > 0 && ra > 0 ? min(ra, reg_rank) : 0;
-    const int ad = r > 0 ? ad0 : -1;
-    for (int p = ps + tid; p < pe; p += 256) a.pos_info[p] = make_int4(s, ad, r, __float_as_int(r > 0 ? scl : 0.f));
+    const int ad = r_eff > 0 ? ad0 : -1;
+    for (int p = ps + tid; p < pe; p += 256) a.pos_info[p] = make_int4(s, ad, r_eff, __float_as_int(r_eff > 0 ? scl : 0.f));
+    if (fused) {   // v_fin columns [ra, r_ws) of the item's positions
+      const int nz = a.r_ws - ra;
+      for (int e = tid; e < (pe - ps) * nz; e += 256) a.v_fin[(long long)(ps + e / nz) * a.r_ws + ra + e % nz] = 0.f;
+    }
   };
   if (ra == 0) {
     write_pos();
@@ -210,7 +219,10 @@ __global__ __launch_bounds__(256) void k_shrink2(LinearArgs a) {
           const float sum = ((red[0][l][q] + red[1][l][q]) + red[2][l][q]) + red[3][l][q];
           const int p = pg + rb * 16 + 4 * (l / 16) + v;
           const int j = jg + cb * 16 + (l % 16);
-          if (p < pe && j < ra) a.v_part[((long long)c * T + p) * a.r_ws + j] = sum;
+          if (p < pe && j < ra) {
+            if (fused) a.v_fin[(long long)p * a.r_ws + j] = j < r_eff ? scl * sum : 0.f;
+            else a.v_part[((long long)c * T + p) * a.r_ws + j] = sum;
+          }
         }
       }
       __syncthreads();
@@ -771,8 +783,10 @@ void launch_linear_bf16(const LinearArgs& a, hipStream_t st) {
       else if (rmax <= 32) hipLaunchKernelGGL((k_shrink2<1, 2>), grid, dim3(256), lds, st, a);
       else hipLaunchKernelGGL((k_shrink2<1, 4>), grid, dim3(256), lds, st, a);
     }
-    const int n4 = a.T * (a.r_ws / 4);
-    hipLaunchKernelGGL(k_vfinal, dim3((n4 + 255) / 256), dim3(256), 0, st, a);
+    if (a.ks > 1) {
+      const int n4 = a.T * (a.r_ws / 4);
+      hipLaunchKernelGGL(k_vfinal, dim3((n4 + 255) / 256), dim3(256), 0, st, a);
+    }
   }
   auto tiles = [&](int br, int bt) {
     return (long long)((a.d_out + br - 1) / br) * ((a.T + bt - 1) / bt);

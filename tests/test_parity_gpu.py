@@ -183,6 +183,10 @@ _FORCED_SHAPES = [
     # rank chunks wider than 64 columns: max rank 80 (a 64 + 16 split) and 256
     (86, 512, 200, [0] * 30 + [1] * 20 + [2] * 14, {0: 80, 1: 40, 2: 72}),
     (87, 256, 136, [-1] * 3 + [0] * 25 + [1] * 36 + [2] * 3, {0: 256, 1: 100, 2: 1}),
+    # short segments of mixed rank <= 16 over 100 tokens: the unsplit shrink
+    # that writes the final scaled v (zero past each segment's rank)
+    (88, 1024, 1000, sorted(np.random.default_rng(88).integers(-1, 50, size=100).tolist()),
+     {a: [8, 16, 4, 12][a % 4] for a in range(50)}),
 ]
 
 
