@@ -708,33 +708,47 @@ void k_gemm2(LinearArgs a) {
   }
 
   // ---- store y (bf16, RNE), rows scattered through token_index ------------
-  uint16_t* __restrict__ y = (uint16_t*)a.y;
+  // A lane's accumulators are 16 d_out values of one position in runs of 4,
+  // so a direct store would touch 32 rows of y with 16 bytes each per
+  // instruction. They pass through a wave-private LDS tile [position][WR]
+  // instead, and leave as 16-byte pieces with consecutive lanes covering one
+  // row of y (whole 64-256 byte runs).
+  constexpr int YP = WR * 2 + 16;                       // tile row pitch (bytes)
+  constexpr int CPR = WR / 8;                           // 16-byte pieces per row
+  static_assert(C::NW * WT * YP <= C::LDS_BYTES, "y tile fits the LDS");
+  if (a.lora_on) __syncthreads();                       // the expand's LDS reads are done
+  char* yt = (char*)lds + wave * WT * YP;
 #pragma unroll
-  for (int n = 0; n < C::MT; ++n) {
-    const int p = t0 + wt * WT + n * 32 + l32;
-    if (p >= T) continue;
-    int row = a.sv.token_index ? a.sv.token_index[p] : p;
-    row = min(max(row, 0), T - 1);
-    uint16_t* yr = y + (long long)row * d_out;
+  for (int n = 0; n < C::MT; ++n)
 #pragma unroll
-    for (int m = 0; m < C::MR; ++m) {
+    for (int m = 0; m < C::MR; ++m)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int nb = r0 + wr * WR + m * 32 + 8 * q + 4 * (lane / 32);
-        float av[4];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) av[v] = acc[m][n][4 * q + v];
-        if (nb + 3 < d_out && (d_out & 3) == 0) {
-          u32x2_t pk;
-          pk.x = (uint32_t)f32_to_bf16_bits(av[0]) | ((uint32_t)f32_to_bf16_bits(av[1]) << 16);
-          pk.y = (uint32_t)f32_to_bf16_bits(av[2]) | ((uint32_t)f32_to_bf16_bits(av[3]) << 16);
-          *(u32x2_t*)(yr + nb) = pk;
-        } else {
-#pragma unroll
-          for (int v = 0; v < 4; ++v)
-            if (nb + v < d_out) yr[nb + v] = f32_to_bf16_bits(av[v]);
-        }
+        const int rr = m * 32 + 8 * q + 4 * (lane / 32);
+        u32x2_t pk;
+        pk.x = (uint32_t)f32_to_bf16_bits(acc[m][n][4 * q]) | ((uint32_t)f32_to_bf16_bits(acc[m][n][4 * q + 1]) << 16);
+        pk.y = (uint32_t)f32_to_bf16_bits(acc[m][n][4 * q + 2]) | ((uint32_t)f32_to_bf16_bits(acc[m][n][4 * q + 3]) << 16);
+        *(u32x2_t*)(yt + (n * 32 + l32) * YP + rr * 2) = pk;
       }
+  // (wave-private tile: the wave's own LDS writes are ordered before its reads)
+  uint16_t* __restrict__ y = (uint16_t*)a.y;
+  const int col = r0 + wr * WR + 8 * (lane % CPR);
+  const bool vec = (d_out & 7) == 0 && col + 8 <= d_out;
+#pragma unroll 4
+  for (int tb = 0; tb < WT; tb += kWave / CPR) {
+    const int tl = tb + lane / CPR;
+    const int p = t0 + wt * WT + tl;
+    if (p >= T || col >= d_out) continue;
+    int row = a.sv.token_index ? a.sv.token_index[p] : p;
+    row = min(max(row, 0), T - 1);
+    const u32x4_t v = *(const u32x4_t*)(yt + tl * YP + (lane % CPR) * 16);
+    uint16_t* dst = y + (long long)row * d_out + col;
+    if (vec) {
+      *(u32x4_t*)dst = v;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (col + e < d_out) dst[e] = (uint16_t)(v[e / 2] >> (16 * (e & 1)));
     }
   }
 }
