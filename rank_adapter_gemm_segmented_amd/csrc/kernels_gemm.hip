@@ -73,11 +73,19 @@ __global__ __launch_bounds__(256) void k_shrink2(LinearArgs a) {
   __shared__ float red[4][kWave][NQ + 1];
 
   // ---- which (segment, block) is this item? --------------------------------
-  for (int i = tid; i <= S; i += 256) {
-    sst[i] = sv.seg_start[i];
-    if (meta_lds && i < S) {
-      sad[i] = sv.seg_adapter[i];
-      srk[i] = sv.seg_rank ? sv.seg_rank[i] : 0;
+  // All of a round's loads are issued before its LDS stores: the metadata
+  // pointers are generic, so a store placed between them would make every
+  // load wait for the one before it.
+  for (int i0 = 0; i0 <= S; i0 += 256) {
+    const int i = i0 + tid;
+    const bool in = i <= S, meta = meta_lds && i < S;
+    const int st = in ? sv.seg_start[i] : 0;
+    const int ad = meta ? sv.seg_adapter[i] : 0;
+    const int rk = meta && sv.seg_rank ? sv.seg_rank[i] : 0;
+    if (in) sst[i] = st;
+    if (meta) {
+      sad[i] = ad;
+      srk[i] = rk;
     }
   }
   if (tid == 0) found[0] = -1;
@@ -124,16 +132,27 @@ __global__ __launch_bounds__(256) void k_shrink2(LinearArgs a) {
   const int rk0 = meta_lds ? srk[s] : (sv.seg_rank ? sv.seg_rank[s] : 0);
   const bool adok = ad0 >= 0 && ad0 < a.pv.capacity;
   const int ra = adok ? min(max(rk0, 0), a.pv.max_rank) : 0;
-  const int reg_rank = a.pv.rank[adok ? ad0 : 0];
-  const float scl = sv.seg_scale[s];
-  // rank the expand applies: the segment's, capped by the registered one
-  const int r_eff = adok && reg_rank > 0 && ra > 0 ? min(ra, reg_rank) : 0;
+  // The registered rank and the scale are only needed once the first sums
+  // exist. Their loads are vector loads (offset vz is zero but held in a
+  // vector register; a scalar load's wait would come with the next LDS wait),
+  // issued now and consumed after the first k-loop (the asm pins their use
+  // there), so the A and x loads do not wait behind them.
+  int vz;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(vz));
+  int reg_rank = a.pv.rank[(adok ? ad0 : 0) + vz];
+  float scl = sv.seg_scale[s + vz];
+  int r_eff = 0;   // rank the expand applies: the segment's, capped by the registered one
+  auto resolve = [&]() {
+    asm volatile("" : "+v"(reg_rank), "+v"(scl));
+    r_eff = adok && reg_rank > 0 && ra > 0 ? min(ra, reg_rank) : 0;
+  };
   // With one d_in chunk (ks == 1) the sum is final: this kernel writes
   // v_fin = scale * v itself (zero past r_eff, up to the row pitch) and no
   // finalize launch follows.
   const bool fused = a.ks == 1;
   auto write_pos = [&]() {
     if (c != 0) return;
+    resolve();
     const int ad = r_eff > 0 ? ad0 : -1;
     for (int p = ps + tid; p < pe; p += 256) a.pos_info[p] = make_int4(s, ad, r_eff, __float_as_int(r_eff > 0 ? scl : 0.f));
     if (fused) {   // v_fin columns [ra, r_ws) of the item's positions
@@ -159,12 +178,19 @@ __global__ __launch_bounds__(256) void k_shrink2(LinearArgs a) {
 
   for (int pg = ps; pg < pe; pg += 16 * NRB) {
     // x rows of this position group (fixed over k); absent positions read zeros
+    // (gathered rows: every index load is issued before any is used)
     const uint16_t* xrow[NRB];
+    int prow[NRB];
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) prow[rb] = min(pg + rb * 16 + l16, pe - 1);
+    if (sv.token_index) {   // uniform
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) prow[rb] = sv.token_index[prow[rb]];
+    }
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
       const int p = pg + rb * 16 + l16;
-      int row = p < pe ? (sv.token_index ? sv.token_index[p] : p) : 0;
-      row = min(max(row, 0), T - 1);
+      const int row = min(max(prow[rb], 0), T - 1);
       xrow[rb] = p < pe ? x + (long long)row * d_in : nullptr;
     }
     const int nrb = min(NRB, (pe - pg + 15) / 16);
@@ -203,6 +229,7 @@ __global__ __launch_bounds__(256) void k_shrink2(LinearArgs a) {
           load(u, i0 + u + D);   // past the end: zero-block reads
         }
       }
+      resolve();
       // fixed-order sum of the four waves, spread over all threads: entry
       // e = (q, l) is accumulator value q of lane l
 #pragma unroll

@@ -187,6 +187,9 @@ _FORCED_SHAPES = [
     # that writes the final scaled v (zero past each segment's rank)
     (88, 1024, 1000, sorted(np.random.default_rng(88).integers(-1, 50, size=100).tolist()),
      {a: [8, 16, 4, 12][a % 4] for a in range(50)}),
+    # T > 128 on the direct-to-LDS GEMM ring with a d_in tail (1000 = 15 * 64 + 40)
+    (89, 1000, 700, sorted(np.random.default_rng(89).integers(-1, 12, size=200).tolist()),
+     {a: [8, 16, 32, 64][a % 4] for a in range(12)}),
 ]
 
 
