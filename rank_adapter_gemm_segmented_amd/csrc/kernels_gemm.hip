@@ -448,19 +448,6 @@ void k_gemm2(LinearArgs a) {
       for (int n = 0; n < C::MT; ++n)
         fb[n] = *(const u32x4_t*)(Ls + (BR + wt * WT + n * 32 + l32) * C::RB + fcol[kk]);
     };
-    if constexpr (C::MR * C::MT >= 16) {
-      // 128x128 per wave: its 16 MFMAs per k-step cover the LDS latency of the
-      // step's own reads; one fragment set leaves registers for the epilogue
-#pragma unroll
-      for (int kk = 0; kk < KB / 16; ++kk) {
-        frag(kk, af[0], bf[0]);
-#pragma unroll
-        for (int m = 0; m < C::MR; ++m)
-#pragma unroll
-          for (int n = 0; n < C::MT; ++n) acc[m][n] = mfma32g(af[0][m], bf[0][n], acc[m][n]);
-      }
-      return;
-    }
     frag(0, af[0], bf[0]);
 #pragma unroll
     for (int kk = 0; kk < KB / 16; ++kk) {
