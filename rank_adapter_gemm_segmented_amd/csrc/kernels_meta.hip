@@ -46,72 +46,104 @@ void launch_token_map(const int32_t* seg_start, const int32_t* seg_adapter, int 
 // Sorted position of token t = #{t' : id[t'] < id[t]} + #{t' < t : id[t'] == id[t]},
 // i.e. a stable grouping by ascending id (-1 first). The count is exact integer
 // work, so the result is unique and independent of thread scheduling. Then a
-// block scan over "segment starts" numbers the segments.
+// scan over "segment starts" numbers the segments.
+//
+// Latency: every global load happens up front (ids, then each token's
+// registered rank and scale); the sort, the segment flags and the scan stay in
+// LDS (one wave-level scan, one cross-wave step).
 // ---------------------------------------------------------------------------
 constexpr int kSegThreads = 1024;
+constexpr int kSegPerThread = MLORA_MAX_UNSORTED_TOKENS / kSegThreads;   // tokens per thread (8)
 
 __global__ __launch_bounds__(kSegThreads) void k_build_segments(
     const int32_t* __restrict__ token_adapter, const float* __restrict__ adapter_scale, int T,
     PoolView pv, int32_t* __restrict__ token_index, int32_t* __restrict__ seg_start,
     int32_t* __restrict__ seg_adapter, int32_t* __restrict__ seg_rank,
     float* __restrict__ seg_scale, int32_t* __restrict__ n_seg_out) {
-  extern __shared__ int32_t ids[];  // [T] ids in batch order
-  __shared__ int32_t part[kSegThreads];
-  const int tid = threadIdx.x;
+  // LDS: ids [T] (batch order), srt [T] (sorted position -> batch row),
+  // trk [T] and tsc [T] (registered rank and scale of each batch row's adapter)
+  extern __shared__ int32_t sm[];
+  int32_t* ids = sm;
+  int32_t* srt = sm + T;
+  int32_t* trk = sm + 2 * T;
+  float* tsc = (float*)(sm + 3 * T);
+  __shared__ int wtot[kSegThreads / kWave];
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
 
-  for (int t = tid; t < T; t += kSegThreads) ids[t] = token_adapter[t];
-  __syncthreads();
-
-  for (int t = tid; t < T; t += kSegThreads) {
-    const int key = ids[t];
-    int pos = 0;
-    for (int u = 0; u < T; ++u) {
-      const int o = ids[u];
-      pos += (o < key) | ((o == key) & (u < t));
+  // ---- ids, ranks, scales: token t = tid + kSegThreads * i -----------------
+  int key[kSegPerThread];
+#pragma unroll
+  for (int i = 0; i < kSegPerThread; ++i) {
+    const int t = tid + kSegThreads * i;
+    key[i] = t < T ? token_adapter[t] : -1;
+  }
+#pragma unroll
+  for (int i = 0; i < kSegPerThread; ++i) {
+    const int t = tid + kSegThreads * i;
+    const bool valid = key[i] >= 0 && key[i] < pv.capacity;
+    const int r = valid ? pv.rank[key[i]] : 0;
+    const float sc = valid ? adapter_scale[key[i]] : 0.0f;
+    if (t < T) {
+      ids[t] = key[i];
+      trk[t] = r;
+      tsc[t] = sc;
     }
-    token_index[pos] = t;
   }
-  __threadfence_block();
   __syncthreads();
-  // id at sorted position p
-  auto sid = [&](int p) { return ids[token_index[p]]; };
 
-  // each thread owns a contiguous chunk of positions
-  const int chunk = (T + kSegThreads - 1) / kSegThreads;
-  const int pb = tid * chunk;
-  const int pe = min(pb + chunk, T);
-  int cnt = 0;
-  for (int p = pb; p < pe; ++p) cnt += (p == 0 || sid(p) != sid(p - 1));
-  part[tid] = cnt;
-  __syncthreads();
-  // inclusive Hillis-Steele scan over kSegThreads partial counts
-  for (int off = 1; off < kSegThreads; off <<= 1) {
-    int v = tid >= off ? part[tid - off] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
+  // ---- stable rank of every token: G threads share one token's count -------
+  int G = 1;
+  while (G < kWave && T * G * 2 <= kSegThreads) G *= 2;
+  for (int t0 = 0; t0 < T; t0 += kSegThreads / G) {   // uniform
+    const int t = t0 + tid / G, sub = tid % G;
+    const int k = t < T ? ids[t] : 0;
+    int pos = 0;
+    if (t < T)
+      for (int u = sub; u < T; u += G) {
+        const int o = ids[u];
+        pos += (o < k) | ((o == k) & (u < t));
+      }
+    for (int off = 1; off < G; off <<= 1) pos += __shfl_xor(pos, off, kWave);
+    if (t < T && sub == 0) {
+      srt[pos] = t;
+      token_index[pos] = t;
+    }
   }
-  int s = part[tid] - cnt;  // exclusive prefix = index of this chunk's first new segment
+  __syncthreads();
+
+  // ---- segment starts: thread owns positions [pb, pe) ----------------------
+  const int chunk = (T + kSegThreads - 1) / kSegThreads;
+  const int pb = min(tid * chunk, T), pe = min(pb + chunk, T);
+  int cnt = 0;
+  for (int p = pb; p < pe; ++p) cnt += (p == 0 || ids[srt[p]] != ids[srt[p - 1]]);
+  int inc = cnt;   // inclusive scan: the wave, then the waves before it
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int up = __shfl_up(inc, off, kWave);
+    if (lane >= off) inc += up;
+  }
+  if (lane == kWave - 1) wtot[wave] = inc;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += wtot[w];
+  int s = before + inc - cnt;   // index of this thread's first new segment
   for (int p = pb; p < pe; ++p) {
-    if (p == 0 || sid(p) != sid(p - 1)) {
-      const int key = sid(p);
-      const bool valid = key >= 0 && key < pv.capacity;
-      const int r = valid ? pv.rank[key] : 0;
+    const int t = srt[p];
+    if (p == 0 || ids[t] != ids[srt[p - 1]]) {
       seg_start[s] = p;
-      seg_adapter[s] = key;
-      seg_rank[s] = r;
-      seg_scale[s] = valid ? adapter_scale[key] : 0.0f;
+      seg_adapter[s] = ids[t];
+      seg_rank[s] = trk[t];
+      seg_scale[s] = tsc[t];
       ++s;
     }
   }
-  if (tid == kSegThreads - 1) {
-    const int S = part[kSegThreads - 1];
-    seg_start[S] = T;
-    n_seg_out[0] = S;
+  if (tid == kSegThreads - 1) {   // the last thread holds the total
+    seg_start[s] = T;
+    n_seg_out[0] = s;
   }
 }
 
-size_t build_segments_lds_bytes(int T) { return (size_t)T * sizeof(int32_t); }
+size_t build_segments_lds_bytes(int T) { return (size_t)4 * T * sizeof(int32_t); }
 
 void launch_build_segments(const int32_t* token_adapter, const float* adapter_scale, int T,
                            const PoolView& pv, int32_t* token_index, int32_t* seg_start,

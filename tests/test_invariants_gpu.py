@@ -156,3 +156,26 @@ def test_host_validation_errors():
     # re-register after unregister (hot swap)
     dc.pool.register(0, A, B)
     assert dc.pool.rank(0) == 8
+
+
+@pytest.mark.gpu
+def test_build_segments_at_the_token_limit():
+    # the largest unsorted batch the library accepts (the segmentation kernel
+    # keeps four ints per token in LDS): integer outputs bit for bit
+    import rank_adapter_gemm_segmented_amd as ml
+    T = 8192   # MLORA_MAX_UNSORTED_TOKENS
+    rng = np.random.default_rng(61)
+    ids = rng.integers(-1, 300, size=T).tolist()
+    ranks = {a: [8, 16, 32][a % 3] for a in range(300)}
+    log(f"[parity] build_segments at T={T}")
+    c = make_custom_case(61, "bf16", 64, 64, ids, ranks, sorted_input=False)
+    dc = DeviceCase(c)
+    ti, ss, sa, sr, sc, ns = ml.build_segments(dc.token_adapter, dc.adapter_scale, dc.pool)
+    torch.cuda.synchronize()
+    o_ti, o_ss, o_sa = oracle.segment(c.token_adapter, c.capacity)
+    S = int(ns.item())
+    assert S == len(o_sa)
+    assert np.array_equal(ti.cpu().numpy(), o_ti)
+    assert np.array_equal(ss[:S + 1].cpu().numpy(), o_ss)
+    assert np.array_equal(sa[:S].cpu().numpy(), o_sa)
+    assert np.array_equal(sr[:S].cpu().numpy(), np.array([c.adapters[a].rank if a >= 0 else 0 for a in o_sa]))
