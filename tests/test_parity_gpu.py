@@ -204,3 +204,18 @@ def test_forced_paths(path, idx, monkeypatch):
     dc = DeviceCase(c)
     check_case(dc, 1, what=f"forced {path} lora_on=1")
     check_case(dc, 0, what=f"forced {path} lora_on=0")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("T", [1536, 160])
+def test_mid_size_batches(T):
+    # T = 1536 at 4096 outputs takes the 128-row direct-to-LDS GEMM tile; T =
+    # 160 the 64x128 one across two token tiles. d_in = 328 leaves a k tail.
+    rng = np.random.default_rng(90 + T)
+    ids = sorted(rng.integers(-1, 40, size=T).tolist())
+    ranks = {a: [16, 64, 8, 32][a % 4] for a in range(40)}
+    log(f"[parity] mid-size batch T={T}: 328->4096")
+    c = make_custom_case(90 + T, "bf16", 328, 4096, ids, ranks)
+    dc = DeviceCase(c)
+    check_case(dc, 1, sample_rows(c, 48), what=f"mid-size T={T} lora_on=1")
+    check_case(dc, 0, sample_rows(c, 16, seed=1), what=f"mid-size T={T} lora_on=0")
