@@ -124,15 +124,32 @@ def ingest_counters(workload: str, kernels, fetch_csv: str, write_csv: str) -> d
     return out
 
 
+def shrink_split(case) -> int:
+    """d_in chunks of the bf16 shrink, as the library picks them (api.hip and
+    choose_shrink_split_bf16): one chunk for short segments of rank <= 16, else
+    enough chunks to fill the GPU."""
+    T = case.n_tokens
+    nseg = case.n_seg if case.sorted_input else T   # the host's segment bound
+    if T <= 16 * nseg and case.max_rank <= 16:
+        return 1
+    groups = (case.d_in + 511) // 512
+    items = min(nseg, 16384) + (T + 63) // 64
+    ks = 1
+    while ks < 16 and ks * 2 <= groups and items * ks < 1024:
+        ks *= 2
+    return ks
+
+
 def layer_kernels(case):
     """Kernels of one LoRA-on layer call, run back to back on one stream: the
-    split-K stream + finish pair for T <= 64 in bf16; segment build (unsorted
-    input), shrink, v fold and the tiled GEMM with fused expand above that;
-    shrink + GEMM for fp32."""
+    split-K stream + finish pair for T <= 64 in bf16; above that segment build
+    (unsorted input), the shrink, the v fold (only when the shrink splits d_in)
+    and the tiled GEMM with fused expand; shrink + GEMM for fp32."""
     if case.dtype == "bf16" and case.n_tokens <= 64:
         return ["k_stream_bf16", "k_finish_bf16"]
     if case.dtype == "bf16":
-        return (["k_build_segments"] if not case.sorted_input else []) + ["k_shrink2", "k_vfinal", "k_gemm2"]
+        return ((["k_build_segments"] if not case.sorted_input else []) + ["k_shrink2"] +
+                (["k_vfinal"] if shrink_split(case) > 1 else []) + ["k_gemm2"])
     return ["k_shrink_f32", "k_gemm_f32"]
 
 
