@@ -51,11 +51,6 @@ __device__ __forceinline__ long long part_off(int c, int i, int rb, int tb, int 
   return ((((long long)c * n_tiles + i) * 4 + rb) * ntb + tb) * 256;
 }
 
-// Loads below are unconditional from clamped addresses, with the value
-// selected afterwards: branch-free code keeps the compiler's vmcnt waits exact,
-// so MFMAs start on the first W k-step while later ones are still in flight.
-__device__ __forceinline__ u32x4_t sel(bool keep, u32x4_t v) { return keep ? v : zero_u32x4(); }
-
 // Workgroup barrier for LDS data only: waits for this wave's LDS (and scalar)
 // operations, not for its outstanding global loads, which __syncthreads
 // would wait for too. The memory clobber keeps the compiler from moving

@@ -2,24 +2,26 @@
 //
 // y_i = W x_i + scale_s * B_a (A_a x_i) ("Multi-LoRA Serving in Practice",
 // section "Core Principle", displayed formula), per adapter segment
-// ("InvisibleLoRA" abstract). Two launches:
+// ("InvisibleLoRA" abstract). Two or three launches:
 //
 //  k_shrink2  v = A_a x per segment, fp32, split over d_in chunks into
 //             deterministic partials; also writes a per-position table
 //             {segment, adapter, rank, scale}; k_vfinal folds the partials in
 //             chunk order and applies the scale (v_fin, read by the epilogue).
+//             With a single chunk the shrink writes v_fin itself.
 //  k_gemm2    W x as a tiled GEMM on v_mfma_f32_32x32x16_bf16: block tile of
 //             BR W rows x BT sorted positions over the whole of d_in, both
-//             operands staged through LDS (double-buffered, 144-byte row pitch
-//             so 16-lane operand reads are conflict-free). The epilogue adds
-//             scale * B_a v on the same accumulators with MFMAs (v split into
-//             a bf16 high and low part, ~16 mantissa bits) and stores y once.
+//             operands staged through LDS (a direct-to-LDS load ring on the
+//             narrow tiles, register staging on the 256x256 one). The
+//             epilogue adds scale * B_a v on the same accumulators with MFMAs
+//             (v split into a bf16 high and low part, ~16 mantissa bits) and
+//             stores y once, through an LDS transpose.
 //
 // MFMA 32x32x16 bf16 layout: lane l supplies row l%32 and k-slots 8*(l/32)..+7
 // of each operand; result register v of lane l is row 8*(v/4)+4*(l/32)+v%4,
 // column l%32. The A operand is W (rows = output features) and the B operand
 // is x (columns = tokens), so each lane ends with runs of 4 consecutive
-// features of one token: 8-byte stores of y.
+// features of one token.
 #include "common.h"
 #include "launch.h"
 
