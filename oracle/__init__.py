@@ -6,7 +6,8 @@ does. It shares no code with the GPU path; the only thing both sides see is the
 seeded input generator in ``mlora_inputs``.
 
 The C source computes the plain per-token definition of the multi-LoRA linear
-layer in double precision (see the header comment of ``mlora_oracle.c``).
+layer in double precision (see the header comment of ``mlora_oracle.c``), and
+the merged weight W + scale * B A of one adapter.
 """
 from __future__ import annotations
 
@@ -81,6 +82,8 @@ def load(path: Optional[str] = None):
         lib.mlo_linear.argtypes = [i32, i32, i32, P, P, i32, P, P, P, P, P, i32, P, P, P, P, P,
                                    i32, i32, P, P, P, i32]
         lib.mlo_linear.restype = i32
+        lib.mlo_merge.argtypes = [i32, i32, i32, P, P, P, ctypes.c_double, P, i32]
+        lib.mlo_merge.restype = i32
         if path is None:
             _lib = lib
         return lib
@@ -193,3 +196,21 @@ def case_linear(case, lora_on: int = 1, rows=None, threads: int = 0, with_base: 
     pool = pool or PackedPool(case.adapters, case.capacity, case.d_in, case.d_out)
     ss, sa, sr, sc, ti = case_metadata(case)
     return linear(case.x, case.W, pool, ss, sa, sr, sc, ti, lora_on, rows, threads, with_base)
+
+
+def merge(W, A, B, scale: float, threads: int = 0, lib=None) -> np.ndarray:
+    """fp64 merged weight W + scale * B A of one adapter (A [r, d_in],
+    B [d_out, r]); a negative scale unmerges. ``scale`` is taken as the
+    float32 value the library receives."""
+    lib = lib or load()
+    W = _c(W, np.float32)
+    d_out, d_in = W.shape
+    A = _c(A, np.float32).reshape(-1, d_in)
+    r = int(A.shape[0])
+    B = _c(B, np.float32).reshape(d_out, r)
+    out = np.zeros((d_out, d_in), np.float64)
+    rc = lib.mlo_merge(d_in, d_out, r, _f32p(W), _f32p(A), _f32p(B),
+                       float(np.float32(scale)), _f64p(out), int(threads))
+    if rc != MLO_OK:
+        raise OracleError(rc, "merge")
+    return out

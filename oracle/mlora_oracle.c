@@ -238,3 +238,40 @@ int mlo_linear(int n_tokens, int d_in, int d_out, const float* x, const float* W
   }
   return err;
 }
+
+/*
+ * Merged weight of one adapter: W_out = W + c * B A.
+ *
+ * The "LoRA Inference" glossary (first paragraph) merges an adapter into the
+ * frozen weights as W = W0 + dW, and its "Model Merging" paragraph combines
+ * adapters by adding them. The update of one adapter is the low-rank term of
+ * the "Multi-LoRA Serving in Practice" LoRA forward (section "Core
+ * Principle", displayed formula): scale times B applied after A, so
+ * dW = c B A. A negative c removes a merged adapter again (unmerge).
+ *
+ * Plain definition in double, one output element at a time, j ascending:
+ *   W_out[n,k] = W[n,k] + c * sum_{j<rank} B[n,j] * A[j,k]
+ * with A [rank, d_in] and B [d_out, rank] row-major. Rows are independent, so
+ * the result does not depend on the number of OpenMP threads.
+ */
+int mlo_merge(int d_in, int d_out, int rank, const float* W, const float* A, const float* B,
+              double c, double* W_out, int n_threads) {
+  if (d_in <= 0 || d_out <= 0 || rank < 0) return MLO_ERR_ARG;
+  if (!W || !W_out || (rank > 0 && (!A || !B))) return MLO_ERR_ARG;
+#ifdef _OPENMP
+  int nt = n_threads > 0 ? n_threads : omp_get_max_threads();
+#pragma omp parallel for num_threads(nt) schedule(static)
+#endif
+  for (int n = 0; n < d_out; ++n) {
+    const float* bn = B + (size_t)n * rank;
+    for (int k = 0; k < d_in; ++k) {
+      double dw = 0.0;
+      for (int j = 0; j < rank; ++j) dw += (double)bn[j] * (double)A[(size_t)j * d_in + k];
+      W_out[(size_t)n * d_in + k] = (double)W[(size_t)n * d_in + k] + c * dw;
+    }
+  }
+#ifndef _OPENMP
+  (void)n_threads;
+#endif
+  return MLO_OK;
+}

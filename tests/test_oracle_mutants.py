@@ -35,6 +35,15 @@ MUTANTS = {
     "rank_from_segment_plus_one": ("const int r = adapter_rank[a];",
                                    "const int r = adapter_rank[a] > 1 ? adapter_rank[a] - 1 : 1;"),
     "lora_on_ignored": ("if (!lora_on) continue;", "(void)0;"),
+    "merge_scale_dropped": ("= (double)W[(size_t)n * d_in + k] + c * dw;",
+                            "= (double)W[(size_t)n * d_in + k] + dw;"),
+    "merge_sign_flipped": ("= (double)W[(size_t)n * d_in + k] + c * dw;",
+                           "= (double)W[(size_t)n * d_in + k] - c * dw;"),
+    "merge_A_transposed_index": ("dw += (double)bn[j] * (double)A[(size_t)j * d_in + k];",
+                                 "dw += (double)bn[j] * (double)A[(size_t)k * rank + j];"),
+    "merge_drops_last_rank_row": ("for (int j = 0; j < rank; ++j) dw +=",
+                                  "for (int j = 0; j + 1 < rank; ++j) dw +="),
+    "merge_drops_W": ("= (double)W[(size_t)n * d_in + k] + c * dw;", "= c * dw;"),
 }
 
 

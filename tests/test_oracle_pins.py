@@ -9,7 +9,8 @@ plausible mistake is caught by at least one of them.
 Sources of the facts pinned:
 * LoRA forward: "Multi-LoRA Serving in Practice", section "Core Principle"
   (displayed formula, base product plus scale times B applied to A x).
-* Merged weights W = W0 + dW: "LoRA Inference" glossary, first paragraph.
+* Merged weights W = W0 + dW: "LoRA Inference" glossary, first paragraph
+  (pinned for the layer and for the oracle's merge of one adapter).
 * LoRA-off pass = base model alone; batch partitioned across adapters:
   "InvisibleLoRA" abstract.
 * Grouping same-adapter requests: "Multi-LoRA Serving in Practice",
@@ -267,9 +268,75 @@ def pin_token_map(lib):
         assert ta.tolist() == [int(sa[s]) for s in exp_s]
 
 
+# ---- merged weight W + c B A of one adapter (oracle.merge) ----------------
+# "LoRA Inference" glossary, first paragraph: W = W0 + dW; dW = c B A is the
+# low-rank term of the "Multi-LoRA Serving in Practice" LoRA forward.
+
+def _merge_inputs(seed, d_in, d_out, r):
+    rng = np.random.default_rng(seed)
+    W = rng.normal(0, 0.02, (d_out, d_in)).astype(np.float32)
+    A = rng.normal(0, 0.02, (r, d_in)).astype(np.float32)
+    B = rng.normal(0, 0.01, (d_out, r)).astype(np.float32)
+    return W, A, B
+
+
+def pin_merge_is_library_product(lib):
+    # a numpy fp64 matrix product of B and A, added to W
+    for seed, (d_in, d_out, r, c) in enumerate([(40, 24, 5, 2.0), (17, 33, 1, -0.75), (64, 8, 16, 0.3)]):
+        W, A, B = _merge_inputs(200 + seed, d_in, d_out, r)
+        m = oracle.merge(W, A, B, c, lib=lib)
+        ref = W.astype(np.float64) + np.float64(np.float32(c)) * (B.astype(np.float64) @ A.astype(np.float64))
+        assert _rel_err(m, ref) < 1e-12, seed
+
+
+def pin_merge_serves_like_adapter(lib):
+    # a batch whose every token uses adapter a with scale c gives the same y
+    # through the layer (LoRA-on) as through the merged weight alone
+    rng = np.random.default_rng(9)
+    for trial in range(3):
+        T, d_in, d_out, r = int(rng.integers(1, 9)), int(rng.integers(2, 49)), int(rng.integers(2, 49)), int(rng.integers(1, 9))
+        c = float(rng.normal())
+        case = make_custom_case(300 + trial, "f32", d_in, d_out, [0] * T, {0: r}, scales={0: c})
+        pool = _pool(case.adapters, case.capacity, d_in, d_out)
+        y = oracle.linear(case.x, case.W, pool, case.seg_start, case.seg_adapter, case.seg_rank,
+                          case.seg_scale, None, 1, lib=lib)
+        m = oracle.merge(case.W, case.adapters[0].A, case.adapters[0].B, c, lib=lib)
+        assert _rel_err(case.x.astype(np.float64) @ m.T, y) < 1e-12, trial
+
+
+def pin_merge_closed_forms(lib):
+    d_in, d_out = 12, 10
+    W, _, _ = _merge_inputs(7, d_in, d_out, 1)
+    # rank one with A = e_k^T, B = e_n: only W[n, k] moves, by exactly c
+    for (n, k, c) in [(0, 0, 1.5), (9, 11, -2.0), (3, 7, 0.25)]:
+        A = np.zeros((1, d_in), np.float32)
+        A[0, k] = 1
+        B = np.zeros((d_out, 1), np.float32)
+        B[n, 0] = 1
+        m = oracle.merge(W, A, B, c, lib=lib)
+        ref = W.astype(np.float64)
+        ref[n, k] += c
+        assert np.array_equal(m, ref), (n, k)
+    # c = 0 or B = 0 leave W exactly
+    _, A, B = _merge_inputs(8, d_in, d_out, 4)
+    assert np.array_equal(oracle.merge(W, A, B, 0.0, lib=lib), W.astype(np.float64))
+    assert np.array_equal(oracle.merge(W, A, np.zeros_like(B), 3.0, lib=lib), W.astype(np.float64))
+
+
+def pin_merge_unmerge_and_linearity(lib):
+    W, A, B = _merge_inputs(11, 30, 20, 6)
+    m1 = oracle.merge(W, A, B, 1.0, lib=lib)
+    m2 = oracle.merge(W, A, B, 2.0, lib=lib)
+    assert _rel_err(m2 - W, 2.0 * (m1 - W)) < 1e-12
+    back = oracle.merge(m1.astype(np.float32), A, B, -1.0, lib=lib)
+    # m1 rounded to float32 before unmerging: back to W within float32 rounding of m1
+    assert np.max(np.abs(back - W)) <= 2.0 ** -24 * np.max(np.abs(m1)) * 2
+
+
 PINS = [pin_hand_example, pin_base_is_library_product, pin_lora_term_is_library_product,
         pin_merged_weights, pin_vanishing_terms, pin_one_hot_and_rank_one, pin_permutation,
-        pin_linearity, pin_segmentation_exhaustive, pin_token_map]
+        pin_linearity, pin_segmentation_exhaustive, pin_token_map, pin_merge_is_library_product,
+        pin_merge_serves_like_adapter, pin_merge_closed_forms, pin_merge_unmerge_and_linearity]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
