@@ -60,8 +60,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_bf16",
-                    choices=["decode_bf16", "verify_bf16", "hetero_bf16", "prefill_bf16", "tiny_f32"])
-    ap.add_argument("--proj", default="q", help="prefill projection")
+                    choices=["decode_bf16", "verify_bf16", "hetero_bf16", "prefill_bf16", "tiny_f32",
+                             "merge_bf16"])
+    ap.add_argument("--proj", default="q", help="prefill projection (also the merge shape)")
+    ap.add_argument("--rank", type=int, default=64, help="adapter rank of the merge workload")
     ap.add_argument("--rotate-gib", type=float, default=1.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -153,6 +155,104 @@ def layer_kernels(case):
     return ["k_shrink_f32", "k_gemm_f32"]
 
 
+def bench_merge(args):
+    """Merge of one adapter into a base weight, W_out = W_in + scale * B A
+    (out of place), for one decoder-layer projection shape. Algorithmic bytes:
+    W read + W_out written + A and B read once."""
+    import numpy as np
+    import torch
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import rank_adapter_gemm_segmented_amd as ml
+    from gpu_util import to_dev
+    from mlora_inputs import PREFILL_SHAPES, make_merge_inputs
+
+    d_in, d_out = PREFILL_SHAPES[args.proj]
+    r = args.rank
+    name = f"merge_bf16_{args.proj}_r{r}"
+    torch.cuda.set_device(0)
+    W, ad = make_merge_inputs(2000 + r, "bf16", d_in, d_out, r)
+    W0 = to_dev(W, "bf16")
+    pool0 = ml.Pool(d_in, d_out, torch.bfloat16, r, 1)
+    pool0.register(0, to_dev(ad.A, "bf16"), to_dev(ad.B, "bf16"))
+    es = 2
+    alg = 2 * d_out * d_in * es + r * (d_in + d_out) * es
+    set_bytes = 2 * W0.numel() * es + pool0.arena.numel()
+    n_sets = 2 if args.profile else max(2, int(np.ceil(args.rotate_gib * (1 << 30) / set_bytes)))
+    sets = []
+    for i in range(n_sets):
+        if i == 0:
+            Wi, pool = W0, pool0
+        else:
+            Wi = W0.clone()
+            pool = ml.Pool(d_in, d_out, torch.bfloat16, r, 1)
+            pool.register(0, to_dev(ad.A, "bf16"), to_dev(ad.B, "bf16"))
+        sets.append((Wi, torch.empty_like(Wi), pool))
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def run(steps, warmup):
+        for i in range(warmup):
+            Wi, Wo, pool = sets[i % n_sets]
+            ml.merge_adapter(Wi, pool, 0, 2.0, out=Wo)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps):
+            Wi, Wo, pool = sets[i % n_sets]
+            ml.merge_adapter(Wi, pool, 0, 2.0, out=Wo)
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    if args.profile:
+        run(5, 2)
+        print(f"[bench] {name}: 7 merge calls done", file=sys.stderr, flush=True)
+        n = 256 << 20
+        src = torch.ones(n // 2, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] calibration copy of {n} bytes done", file=sys.stderr, flush=True)
+        return
+    ms = run(args.steps, args.warmup)
+    gbs = alg / (ms * 1e-3) / 1e9
+    print(f"[bench] {name}: {ms * 1e3:.2f} us/call, {n_sets} buffer sets of {set_bytes / 2**20:.1f} MiB",
+          file=sys.stderr, flush=True)
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = max(1, min(len(os.sched_getaffinity(0)), 16))
+        rows = max(1, min(d_out, int(2e9 / (d_in * r))))   # a bounded prefix of W's rows
+        reps, t_total = 0, 0.0
+        while t_total * threads < args.cpu_seconds or reps == 0:
+            t0 = time.perf_counter()
+            oracle.merge(W[:rows], ad.A, ad.B[:rows], 2.0, threads=threads)
+            t_total += time.perf_counter() - t0
+            reps += 1
+            if reps >= 50:
+                break
+        t_full = t_total / reps * (d_out / rows)
+        cpu = {"value": round(alg / t_full / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+               "sample": f"{rows} of {d_out} rows of W, fp64, {reps} repetitions, {t_total:.1f} s wall; "
+                         f"value scaled to the whole weight",
+               "seconds_per_merge": round(t_full, 4)}
+    out = {
+        "metric": "adapter merge W + scale*B*A, effective HBM GB/s (% roofline)",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded Gaussian weight and adapter)",
+        "config": {"workload": name, "d_in": d_in, "d_out": d_out, "rank": r, "buffer_sets": n_sets,
+                   "algorithmic_bytes": alg},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "algorithmic_bytes": alg,
+                     "us_per_call": round(ms * 1e3, 3), "kernels": ["k_merge_bf16"],
+                     "kernel_source_hash": kernel_source_hash()},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -160,6 +260,9 @@ def main():
         print("bench.py measures one GPU only: this layer is built and timed on a single MI355X "
               "(no sharding or collectives); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "merge_bf16":
+        bench_merge(args)
+        return
 
     import numpy as np
     import torch

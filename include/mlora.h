@@ -194,6 +194,28 @@ int mlora_validate(mlora_pool_t pool, const int32_t* seg_start, const int32_t* s
                    const int32_t* seg_rank, const int32_t* token_index, int n_tokens, int n_seg,
                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Merged weights
+ * ---------------------------------------------------------------------- */
+
+/* Merge registered adapter `adapter_id` into a base weight:
+ *
+ *     W_out = W_in + scale * B_a A_a          (W_in, W_out [d_out, d_in], pool dtype)
+ *
+ * The "LoRA Inference" glossary (first paragraph) serves an adapter merged into
+ * the frozen weights, W = W0 + dW, at the base model's cost; dW is the scaled
+ * low-rank term of the LoRA forward ("Multi-LoRA Serving in Practice", section
+ * "Core Principle"). Its "Model Merging" paragraph combines adapters by
+ * adding them: call once per adapter. A negative scale removes a merged
+ * adapter (unmerge). bf16 accumulates dW in fp32 and rounds W_out once per
+ * call (RNE), so unmerging restores W_in only to within that rounding; fp32
+ * adds in fp32. Device pointers; W_out may equal W_in (in place) but must not
+ * otherwise overlap it. Stream-ordered after the adapter's registration.
+ * Errors: MLORA_ERR_INVALID_ARG (null or misaligned pointer, partial overlap),
+ * MLORA_ERR_ADAPTER (id out of range or slot empty). */
+int mlora_merge_adapter(const void* W_in, void* W_out, mlora_pool_t pool, int adapter_id,
+                        float scale, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

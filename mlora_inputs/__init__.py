@@ -42,7 +42,7 @@ import numpy as np
 __all__ = [
     "Adapter", "Case", "bf16_round", "bf16_bits", "bf16_from_bits",
     "make_case", "make_custom_case", "WORKLOADS", "PREFILL_SHAPES",
-    "sorted_metadata", "zipf_probs",
+    "sorted_metadata", "zipf_probs", "make_merge_inputs",
 ]
 
 
@@ -300,3 +300,15 @@ def make_custom_case(seed: int, dtype: str, d_in: int, d_out: int, token_adapter
         ss, sa, sr, sc = sorted_metadata(tok, pool, scale)
         case.seg_start, case.seg_adapter, case.seg_rank, case.seg_scale = ss, sa, sr, sc
     return case
+
+
+def make_merge_inputs(seed: int, dtype: str, d_in: int, d_out: int, rank: int,
+                      sigma_w: float = 0.02, sigma_a: float = 0.02, sigma_b: float = 0.01):
+    """Base weight W [d_out, d_in] and one adapter (A [rank, d_in], B [d_out, rank])
+    for merging, drawn in that order from ``default_rng(seed)`` with the
+    workloads' Gaussian inits, rounded to the storage dtype."""
+    rng = np.random.default_rng(seed)
+    W = _normal(rng, (d_out, d_in), sigma_w, dtype)
+    A = _normal(rng, (rank, d_in), sigma_a, dtype)
+    B = _normal(rng, (d_out, rank), sigma_b, dtype)
+    return W, Adapter(rank, A, B)

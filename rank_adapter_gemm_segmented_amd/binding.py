@@ -55,6 +55,7 @@ def _load() -> ctypes.CDLL:
         "mlora_linear_tokens": ([P, P, P, P, P, I, I, P, P, SZ, P], I),
         "mlora_token_map": ([P, P, I, I, P, P, P], I),
         "mlora_validate": ([P, P, P, P, P, I, I, P, SZ, P], I),
+        "mlora_merge_adapter": ([P, P, P, I, ctypes.c_float, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -234,3 +235,16 @@ def validate(pool: Pool, seg_start, seg_adapter, seg_rank=None, token_index=None
                                    _ptr(_i32(seg_rank, "seg_rank")),
                                    _ptr(_i32(token_index, "token_index")), T,
                                    int(seg_adapter.numel()), _ptr(ws), ws.numel(), _stream()))
+
+
+def merge_adapter(W, pool: Pool, adapter_id: int, scale: float, out=None):
+    """``mlora_merge_adapter``: W + scale * B_a A_a into ``out`` (a new tensor
+    if None; pass ``out=W`` to merge in place). A negative scale unmerges."""
+    if W.dtype != pool.dtype or tuple(W.shape) != (pool.d_out, pool.d_in) or not W.is_contiguous():
+        raise ValueError("W must be a contiguous [d_out, d_in] tensor of the pool's dtype")
+    o = out if out is not None else torch.empty_like(W)
+    if o.dtype != W.dtype or o.shape != W.shape or not o.is_contiguous():
+        raise ValueError("out must match W")
+    _check(_lib.mlora_merge_adapter(_ptr(W), _ptr(o), pool.handle, int(adapter_id), float(scale),
+                                    _stream()), "mlora_merge_adapter")
+    return o

@@ -17,7 +17,8 @@ LIB = os.path.join(HERE, "libmlora.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.hip", "kernels_meta.hip", "kernels_gemm.hip", "kernels_decode.hip", "kernels_f32.hip"]
+SOURCES = ["api.hip", "kernels_meta.hip", "kernels_gemm.hip", "kernels_decode.hip", "kernels_f32.hip",
+           "kernels_merge.hip"]
 
 # Packed fp32 VALU ops are disabled for every device compile.
 FLAGS = [

@@ -375,6 +375,31 @@ int mlora_token_map(const int32_t* seg_start, const int32_t* seg_adapter, int n_
   return check_launch();
 }
 
+int mlora_merge_adapter(const void* W_in, void* W_out, mlora_pool_t pool, int adapter_id,
+                        float scale, hipStream_t stream) {
+  if (!pool || !W_in || !W_out) return MLORA_ERR_INVALID_ARG;
+  if (!aligned16(W_in) || !aligned16(W_out)) return MLORA_ERR_INVALID_ARG;
+  const size_t wbytes = (size_t)pool->d_out * pool->d_in * pool->elem;
+  const uintptr_t wi = (uintptr_t)W_in, wo = (uintptr_t)W_out;
+  if (wi != wo && wi < wo + wbytes && wo < wi + wbytes) return MLORA_ERR_INVALID_ARG;  // partial overlap
+  if (adapter_id < 0 || adapter_id >= pool->capacity) return MLORA_ERR_ADAPTER;
+  const int rank = pool->host_rank[adapter_id];
+  if (rank <= 0) return MLORA_ERR_ADAPTER;
+  const char* slot = (const char*)pool->base + (size_t)adapter_id * (size_t)pool->slot_elems * pool->elem;
+  MergeArgs a;
+  a.W_in = W_in;
+  a.W_out = W_out;
+  a.A = slot;
+  a.B = slot + (size_t)pool->b_offset * pool->elem;
+  a.d_in = pool->d_in;
+  a.d_out = pool->d_out;
+  a.rank = rank;
+  a.pitch = (rank + 7) & ~7;
+  a.scale = scale;
+  launch_merge(a, pool->dtype == MLORA_BF16, stream);
+  return check_launch();
+}
+
 int mlora_validate(mlora_pool_t pool, const int32_t* seg_start, const int32_t* seg_adapter,
                    const int32_t* seg_rank, const int32_t* token_index, int n_tokens, int n_seg,
                    void* workspace, size_t workspace_bytes, hipStream_t stream) {

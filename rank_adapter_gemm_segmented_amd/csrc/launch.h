@@ -51,6 +51,19 @@ struct DecodeArgs {
   int unit_rows;   // rank rows per shrink unit (4, 8 or 16)
 };
 
+// Merge of one adapter into a base weight: W_out = W_in + scale * B A.
+struct MergeArgs {
+  const void* W_in;
+  void* W_out;     // == W_in (in place) or disjoint
+  const void* A;   // slot A [rank, d_in]
+  const void* B;   // slot B [d_out, pitch], zero-padded past the rank
+  int d_in, d_out, rank, pitch;
+  float scale;
+};
+
+// merge kernels (kernels_merge.hip)
+void launch_merge(const MergeArgs& a, bool bf16, hipStream_t st);
+
 // metadata kernels (kernels_meta.hip)
 void launch_token_map(const int32_t* seg_start, const int32_t* seg_adapter, int T, int S,
                       int32_t* token_seg, int32_t* token_adapter, hipStream_t st);
