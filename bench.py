@@ -217,6 +217,19 @@ def bench_merge(args):
         return
     ms = run(args.steps, args.warmup)
     gbs = alg / (ms * 1e-3) / 1e9
+    # reference: a plain device copy of W over the same buffer sets (read + write, no dW)
+    for i in range(args.warmup):
+        sets[i % n_sets][1].copy_(sets[i % n_sets][0])
+    torch.cuda.synchronize()
+    c0 = torch.cuda.Event(enable_timing=True)
+    c1 = torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for i in range(args.steps):
+        sets[i % n_sets][1].copy_(sets[i % n_sets][0])
+    c1.record(stream)
+    c1.synchronize()
+    ms_copy = c0.elapsed_time(c1) / args.steps
+    copy_bytes = 2 * d_out * d_in * es
     print(f"[bench] {name}: {ms * 1e3:.2f} us/call, {n_sets} buffer sets of {set_bytes / 2**20:.1f} MiB",
           file=sys.stderr, flush=True)
     cpu = None
@@ -248,6 +261,9 @@ def bench_merge(args):
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "algorithmic_bytes": alg,
                      "us_per_call": round(ms * 1e3, 3), "kernels": ["k_merge_bf16"],
                      "kernel_source_hash": kernel_source_hash()},
+        "copy_reference": {"us_per_call": round(ms_copy * 1e3, 3),
+                           "gbs": round(copy_bytes / (ms_copy * 1e-3) / 1e9, 1),
+                           "what": "torch copy_ of W into W_out over the same buffer sets"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

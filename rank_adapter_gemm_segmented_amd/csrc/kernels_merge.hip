@@ -8,17 +8,18 @@
 // Principle", displayed formula), so dW = c B A. c < 0 unmerges.
 //
 // bf16 (k_merge_bf16): one workgroup of 4 waves per 64-row x 128-column tile
-// of W. The kernel streams W once in and once out (HBM bound); dW is a
-// K = rank contraction that runs on v_mfma_f32_32x32x16_bf16:
+// of W, 4 waves per SIMD resident. The kernel streams W once in and once out
+// (HBM bound); dW is a K = rank contraction on v_mfma_f32_32x32x16_bf16:
 //  1. each thread requests its four 16-byte pieces of the W tile first;
-//  2. per rank chunk of 64: the B rows of the tile's 64 W rows are loaded
+//  2. per rank chunk of 64: the A chunk [64 rank rows x 128 columns] is
+//     loaded coalesced and stored to LDS as loaded (zero past the rank). An
+//     MFMA operand (8 rank entries of one column) is gathered with 2-byte LDS
+//     reads; a transposed store of 2-byte pieces measured slower, since its
+//     lanes fall on few banks. The B rows of the tile's 64 W rows are loaded
 //     straight into MFMA operand registers (8 consecutive rank entries are
-//     one 16-byte load, since pool B rows are zero-padded to a multiple of
-//     8); the A chunk [64 rank rows x 128 columns] is loaded coalesced and
-//     written to LDS transposed (At[column][rank], zero past the rank), so an
-//     MFMA operand of 8 rank entries is one 16-byte LDS read. Wave w
-//     multiplies columns 32w..32w+31 (MFMA rows) against the tile's two
-//     32-row blocks (MFMA columns);
+//     one 16-byte load: pool B rows are zero-padded to a multiple of 8).
+//     Wave w multiplies columns 32w..32w+31 (MFMA rows) against the tile's
+//     two 32-row blocks (MFMA columns);
 //  3. c * dW (fp32) goes to an LDS tile [64][128]; each thread adds it to its
 //     W pieces in fp32, rounds once (RNE) and stores 16 bytes.
 // MFMA 32x32x16 bf16 layout: lane l supplies row l%32 and k-slots
@@ -40,17 +41,17 @@ namespace {
 constexpr int kMgRows = 64;                  // W rows per tile
 constexpr int kMgCols = 128;                 // W columns per tile
 constexpr int kMgRc = 64;                    // rank rows per chunk
-constexpr int kMgAtPitch = kMgRc + 8;        // bf16 per transposed-A row (144 bytes)
+constexpr int kMgAsPitch = kMgCols + 8;      // bf16 per staged A row (272 bytes)
 constexpr int kMgDPitch = kMgCols + 4;       // floats per delta-tile row
-constexpr int kMgAtBytes = kMgCols * kMgAtPitch * 2;
+constexpr int kMgAsBytes = kMgRc * kMgAsPitch * 2;
 constexpr int kMgDBytes = kMgRows * kMgDPitch * 4;
-constexpr int kMgLds = kMgAtBytes > kMgDBytes ? kMgAtBytes : kMgDBytes;
+constexpr int kMgLds = kMgAsBytes > kMgDBytes ? kMgAsBytes : kMgDBytes;
 
 __device__ __forceinline__ f32x16_t mfma32m(u32x4_t a, u32x4_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
-__global__ __launch_bounds__(256) void k_merge_bf16(MergeArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_merge_bf16(MergeArgs a) {
   __shared__ __align__(16) char lds[kMgLds];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int k0 = blockIdx.x * kMgCols, n0 = blockIdx.y * kMgRows;
@@ -74,20 +75,12 @@ __global__ __launch_bounds__(256) void k_merge_bf16(MergeArgs a) {
   for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[nb][v] = 0.f;
-  uint16_t* At = (uint16_t*)lds;
+  uint16_t* As = (uint16_t*)lds;
   // B rows of this lane's two MFMA columns; rows past d_out are clamped (their results are dropped)
   const int nrow0 = min(n0 + (lane & 31), d_out - 1);
   const int nrow1 = min(n0 + 32 + (lane & 31), d_out - 1);
   for (int jc = 0; jc < rank; jc += kMgRc) {
     const int kr = min(kMgRc, rank - jc);      // rank rows in this chunk
-    u32x4_t bv[4][2];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int jj = jc + 16 * s + 8 * (lane >> 5);
-      const bool on = 16 * s < kr && jj < pitch;
-      bv[s][0] = on ? ld16(B + (long long)nrow0 * pitch + jj) : zero_u32x4();
-      bv[s][1] = on ? ld16(B + (long long)nrow1 * pitch + jj) : zero_u32x4();
-    }
     u32x4_t av[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -96,28 +89,43 @@ __global__ __launch_bounds__(256) void k_merge_bf16(MergeArgs a) {
       const int col = min(k0 + 8 * (idx & 15), d_in - 8);   // columns past d_in are dropped
       av[i] = j < kr ? ld16(A + (long long)(jc + j) * d_in + col) : zero_u32x4();
     }
-    if (jc) __syncthreads();                   // the previous chunk's At reads are done
+    if (jc) __syncthreads();                   // the previous chunk's LDS reads are done
+    // rows of the chunk as loaded (16-byte stores, no bank conflicts); only the
+    // rank rows the MFMAs read (zero from kr up to the next multiple of 16)
+    const int kr16 = (kr + 15) & ~15;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int idx = tid + 256 * i;
-      const int j = idx >> 4, c8 = idx & 15;
+      if (16 * i >= kr16) break;               // rows 16 i .. 16 i + 15 of the chunk
+      *(u32x4_t*)(As + (idx >> 4) * kMgAsPitch + 8 * (idx & 15)) = av[i];
+    }
+    // B operands after the A registers are free (they are L2 hits: every column tile reads them)
+    u32x4_t bv[4][2];
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        At[(8 * c8 + e) * kMgAtPitch + j] = (uint16_t)(av[i][e >> 1] >> (16 * (e & 1)));
+    for (int s = 0; s < 4; ++s) {
+      const int jj = jc + 16 * s + 8 * (lane >> 5);
+      const bool on = 16 * s < kr && jj < pitch;
+      bv[s][0] = on ? ld16(B + (long long)nrow0 * pitch + jj) : zero_u32x4();
+      bv[s][1] = on ? ld16(B + (long long)nrow1 * pitch + jj) : zero_u32x4();
     }
     __syncthreads();
+    const int mcol = 32 * wave + (lane & 31);  // this lane's MFMA row: a W column of the tile
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       if (16 * s >= kr) break;
-      const u32x4_t am =
-          *(const u32x4_t*)(At + (32 * wave + (lane & 31)) * kMgAtPitch + 16 * s + 8 * (lane >> 5));
+      // 8 consecutive rank entries of one column: 2-byte LDS reads down the column
+      const uint16_t* col = As + (16 * s + 8 * (lane >> 5)) * kMgAsPitch + mcol;
+      u32x4_t am;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        am[e] = (uint32_t)col[(2 * e) * kMgAsPitch] | ((uint32_t)col[(2 * e + 1) * kMgAsPitch] << 16);
       acc[0] = mfma32m(am, bv[s][0], acc[0]);
       acc[1] = mfma32m(am, bv[s][1], acc[1]);
     }
   }
 
   // 3. c * dW through LDS, added to the W pieces, one rounding
-  __syncthreads();                             // every wave's At reads are done
+  __syncthreads();                             // every wave's A reads are done
   float* D = (float*)lds;
   const float c = a.scale;
 #pragma unroll
