@@ -61,7 +61,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_bf16",
                     choices=["decode_bf16", "verify_bf16", "hetero_bf16", "prefill_bf16", "tiny_f32",
-                             "merge_bf16"])
+                             "merge_bf16", "fused_qkv_decode", "fused_gateup_verify",
+                             "fused_qkv_prefill", "fused_gateup_prefill"])
     ap.add_argument("--proj", default="q", help="prefill projection (also the merge shape)")
     ap.add_argument("--rank", type=int, default=64, help="adapter rank of the merge workload")
     ap.add_argument("--rotate-gib", type=float, default=1.0)
@@ -269,6 +270,115 @@ def bench_merge(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_fused(args):
+    """Stacked projections (q|k|v or gate|up) in one fused call against the
+    same projections as separate calls, both LoRA-on, over rotating buffer
+    sets. Algorithmic bytes: stacked W + touched adapters' A_m and B_m of
+    every projection + x + y (the zero blocks of the block-diagonal B are not
+    counted)."""
+    import numpy as np
+    import torch
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import rank_adapter_gemm_segmented_amd as ml
+    from gpu_util import f32, i32, to_dev
+    from mlora_inputs import make_fused_case
+
+    torch.cuda.set_device(0)
+    slices = make_fused_case(args.workload)
+    c0 = slices[0]
+    n = len(slices)
+    T, d_in = c0.n_tokens, c0.d_in
+    d_out = sum(c.d_out for c in slices)
+    R = sum(c.max_rank for c in slices)
+    es = 2
+    touched = c0.touched_adapters()
+    alg = (d_out * d_in + T * d_in + T * d_out) * es + sum(
+        (c.adapters[a].rank * d_in + c.d_out * c.adapters[a].rank) * es for c in slices for a in touched)
+    ranks = np.array([c0.adapters[int(a)].rank if a >= 0 else 0 for a in c0.token_adapter])
+    flops = 2.0 * T * d_in * d_out + float(np.sum(2.0 * ranks * (n * d_in + d_out)))
+    x0 = to_dev(c0.x, "bf16")
+    Wf0 = to_dev(np.vstack([c.W for c in slices]), "bf16")
+    meta_f = (i32(c0.seg_start), i32(c0.seg_adapter), i32(np.where(c0.seg_adapter >= 0, c0.seg_rank * n, 0)),
+              f32(c0.seg_scale))
+    meta_s = (i32(c0.seg_start), i32(c0.seg_adapter), i32(c0.seg_rank), f32(c0.seg_scale))
+    dev_ad = {a: [(to_dev(c.adapters[a].A, "bf16"), to_dev(c.adapters[a].B, "bf16")) for c in slices]
+              for a in sorted(c0.adapters)}
+
+    def fused_set(first):
+        W = Wf0 if first else Wf0.clone()
+        pool = ml.Pool(d_in, d_out, torch.bfloat16, R, c0.capacity)
+        for a, sl in dev_ad.items():
+            pool.register_fused(a, sl)
+        return W, pool, torch.empty((T, d_out), dtype=torch.bfloat16, device="cuda"), pool.workspace(T)
+
+    def sep_set():
+        out = []
+        for m, c in enumerate(slices):
+            pool = ml.Pool(d_in, c.d_out, torch.bfloat16, c.max_rank, c.capacity)
+            for a, sl in dev_ad.items():
+                pool.register(a, *sl[m])
+            out.append((to_dev(c.W, "bf16"), pool, torch.empty((T, c.d_out), dtype=torch.bfloat16,
+                                                                device="cuda"), pool.workspace(T)))
+        return out
+
+    set_bytes = 2 * Wf0.numel() * es
+    n_sets = max(2, int(np.ceil(args.rotate_gib * (1 << 30) / set_bytes)))
+    fsets = [fused_set(i == 0) for i in range(n_sets)]
+    ssets = [sep_set() for _ in range(n_sets)]
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def step_fused(i):
+        W, pool, y, ws = fsets[i % n_sets]
+        ml.linear(x0, W, pool, *meta_f, lora_on=1, out=y, workspace=ws)
+
+    def step_sep(i):
+        for W, pool, y, ws in ssets[i % n_sets]:
+            ml.linear(x0, W, pool, *meta_s, lora_on=1, out=y, workspace=ws)
+
+    def timed(fn):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.steps):
+            fn(i)
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    ms_f = timed(step_fused)
+    ms_s = timed(step_sep)
+    gbs = alg / (ms_f * 1e-3) / 1e9
+    print(f"[bench] {args.workload}: fused {ms_f * 1e3:.2f} us/call, separate {ms_s * 1e3:.2f} us "
+          f"({n} calls), {n_sets} buffer sets", file=sys.stderr, flush=True)
+    big = c0.n_tokens > 256
+    roof = ({"bound": "mfma", "achieved": round(flops / (ms_f * 1e-3) / 1e12, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+             "unit": "TFLOP/s", "frac": round(flops / (ms_f * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+            if big else
+            {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": round(gbs / HBM_PEAK_GBS, 4)})
+    roof.update({"traffic": None, "algorithmic_bytes": alg, "us_per_call": round(ms_f * 1e3, 3),
+                 "kernel_source_hash": kernel_source_hash()})
+    out = {
+        "metric": "fused multi-projection multi-LoRA linear, effective GB/s and TFLOP/s; fused vs separate calls",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_f, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded Gaussian weights, adapters and activations)",
+        "config": {"workload": args.workload, "tokens": T, "d_in": d_in,
+                   "d_out_slices": [c.d_out for c in slices], "rank_per_slice": c0.max_rank,
+                   "adapters_touched": len(touched), "segments": c0.n_seg, "buffer_sets": n_sets},
+        "tflops": round(flops / (ms_f * 1e-3) / 1e12, 2),
+        "separate_calls": {"ms_per_step": round(ms_s, 6), "calls": n,
+                           "gbs": round(alg / (ms_s * 1e-3) / 1e9, 1)},
+        "fused_speedup": round(ms_s / ms_f, 4),
+        "roofline": roof,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -278,6 +388,9 @@ def main():
         sys.exit(2)
     if args.workload == "merge_bf16":
         bench_merge(args)
+        return
+    if args.workload.startswith("fused_"):
+        bench_fused(args)
         return
 
     import numpy as np

@@ -108,6 +108,30 @@ int mlora_pool_destroy(mlora_pool_t pool);
 int mlora_register_adapter(mlora_pool_t pool, int adapter_id, int rank, const void* A,
                            const void* B, hipStream_t stream);
 
+/* Register one adapter that targets several projections whose base weights
+ * are stacked into the pool's W, e.g. W = [W_q; W_k; W_v] or [W_gate; W_up]
+ * (an adapter's config lists its target modules, with one rank and one
+ * scaling: "Multi-LoRA Serving in Practice", section "1. Define Adapter
+ * Asset Standards", adapter_config.json). Slice m covers slice_rows[m]
+ * consecutive output rows (the slices in order fill d_out exactly) and carries
+ * A_m [slice_ranks[m], d_in] and B_m [slice_rows[m], slice_ranks[m]].
+ * The slot holds them as one adapter of rank R = sum(slice_ranks):
+ * A = [A_0; A_1; ...] stacked, so one shrink pass over x serves every slice,
+ * and B block-diagonal [d_out, R], so slice m's rows expand only its own
+ * part of v. mlora_linear then computes, for every slice at once,
+ *     y[:, slice m] = W_m x + scale_s * B_m (A_m x)
+ * with one scale per segment shared by the slices. Segments name the
+ * adapter with seg_rank = R. The zero blocks of B are read by the expand
+ * (R / slice rank times the B bytes of separate calls). n_slices in
+ * 1 .. MLORA_MAX_SLICES; slice_rows, slice_ranks, A and B are host arrays
+ * (A[m], B[m] host or device pointers, copied as in mlora_register_adapter).
+ * Errors as mlora_register_adapter, plus MLORA_ERR_SHAPE (slice rows do not
+ * add up to d_out) and MLORA_ERR_RANK (R > max_rank). */
+#define MLORA_MAX_SLICES 8
+int mlora_register_adapter_fused(mlora_pool_t pool, int adapter_id, int n_slices,
+                                 const int* slice_rows, const int* slice_ranks,
+                                 const void* const* A, const void* const* B, hipStream_t stream);
+
 /* Mark a slot empty (stream-ordered). Segments that still name it are
  * reported by mlora_validate and contribute no adapter term. */
 int mlora_unregister_adapter(mlora_pool_t pool, int adapter_id, hipStream_t stream);

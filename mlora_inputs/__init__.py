@@ -42,7 +42,7 @@ import numpy as np
 __all__ = [
     "Adapter", "Case", "bf16_round", "bf16_bits", "bf16_from_bits",
     "make_case", "make_custom_case", "WORKLOADS", "PREFILL_SHAPES",
-    "sorted_metadata", "zipf_probs", "make_merge_inputs",
+    "sorted_metadata", "zipf_probs", "make_merge_inputs", "make_fused_case", "FUSED_WORKLOADS",
 ]
 
 
@@ -312,3 +312,41 @@ def make_merge_inputs(seed: int, dtype: str, d_in: int, d_out: int, rank: int,
     A = _normal(rng, (rank, d_in), sigma_a, dtype)
     B = _normal(rng, (d_out, rank), sigma_b, dtype)
     return W, Adapter(rank, A, B)
+
+
+# Stacked projections served by one fused call: workload -> (batch, projections)
+FUSED_WORKLOADS = {
+    "fused_qkv_decode": ("decode_bf16", ("q", "k", "v")),
+    "fused_gateup_verify": ("verify_bf16", ("gate", "up")),
+    "fused_qkv_prefill": ("prefill_bf16", ("q", "k", "v")),
+    "fused_gateup_prefill": ("prefill_bf16", ("gate", "up")),
+}
+
+
+def make_fused_case(name: str) -> List[Case]:
+    """One Case per stacked projection, all over the same batch.
+
+    The first projection is the batch workload itself (its x, token
+    assignment, segments, scales, and its W and adapters when the shapes
+    agree); every later projection draws its own W [d_out_m, d_in] and, for
+    every pool adapter id in order, A_m [r, d_in] and B_m [d_out_m, r] (same
+    rank as the batch's adapter) from ``default_rng([3000, workload index,
+    m])``. Shapes: ``PREFILL_SHAPES`` (the decode batch's q projection is
+    4096->4096, its k and v 4096->1024; the verify batch's gate and up are
+    4096->14336)."""
+    batch, projs = FUSED_WORKLOADS[name]
+    base = make_case(batch, projs[0])
+    widx = list(FUSED_WORKLOADS).index(name)
+    cases = []
+    for m, proj in enumerate(projs):
+        d_in, d_out = PREFILL_SHAPES[proj]
+        assert d_in == base.d_in
+        if m == 0 and d_out == base.d_out:
+            cases.append(dataclasses.replace(base, name=f"{name}_{proj}"))
+            continue
+        rng = np.random.default_rng([3000, widx, m])
+        W = _normal(rng, (d_out, d_in), 0.02, base.dtype)
+        pool = _make_pool(rng, [(a, base.adapters[a].rank) for a in sorted(base.adapters)],
+                          d_in, d_out, 0.02, 0.01, base.dtype)
+        cases.append(dataclasses.replace(base, name=f"{name}_{proj}", d_out=d_out, W=W, adapters=pool))
+    return cases

@@ -214,3 +214,12 @@ def merge(W, A, B, scale: float, threads: int = 0, lib=None) -> np.ndarray:
     if rc != MLO_OK:
         raise OracleError(rc, "merge")
     return out
+
+
+def fused_case_linear(slice_cases, lora_on: int = 1, rows=None, threads: int = 0):
+    """Oracle output of several projections stacked into one weight: each
+    slice is the plain layer over its own W_m and adapters (A_m, B_m) with the
+    batch's shared segments and scales, and the slices' outputs sit side by
+    side in the order given."""
+    return np.concatenate([case_linear(c, lora_on, rows=rows, threads=threads) for c in slice_cases],
+                          axis=1)

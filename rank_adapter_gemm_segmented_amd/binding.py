@@ -56,6 +56,7 @@ def _load() -> ctypes.CDLL:
         "mlora_token_map": ([P, P, I, I, P, P, P], I),
         "mlora_validate": ([P, P, P, P, P, I, I, P, SZ, P], I),
         "mlora_merge_adapter": ([P, P, P, I, ctypes.c_float, P], I),
+        "mlora_register_adapter_fused": ([P, I, I, P, P, P, P, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -130,6 +131,26 @@ class Pool:
         _check(_lib.mlora_register_adapter(self.handle, adapter_id, rank, _ptr(A), _ptr(B),
                                            _stream()), "mlora_register_adapter")
         # the copy is stream-ordered: keep the sources alive until it has run
+        torch.cuda.current_stream().synchronize()
+
+    def register_fused(self, adapter_id: int, slices):
+        """``mlora_register_adapter_fused``: one adapter over stacked projections.
+        ``slices`` is a list of (A_m [r_m, d_in], B_m [rows_m, r_m]) in the
+        order the projections are stacked in W."""
+        n = len(slices)
+        rows = (ctypes.c_int * n)(*[int(B.shape[0]) for _, B in slices])
+        ranks = (ctypes.c_int * n)(*[int(A.shape[0]) for A, _ in slices])
+        keep = []
+        for A, B in slices:
+            if A.dtype != self.dtype or B.dtype != self.dtype:
+                raise TypeError("adapter dtype differs from the pool dtype")
+            if A.dim() != 2 or A.shape[1] != self.d_in or B.dim() != 2 or B.shape[1] != A.shape[0]:
+                raise ValueError("slice shapes must be A [r, d_in], B [rows, r]")
+            keep.append((A.contiguous(), B.contiguous()))
+        pa = (ctypes.c_void_p * n)(*[A.data_ptr() for A, _ in keep])
+        pb = (ctypes.c_void_p * n)(*[B.data_ptr() for _, B in keep])
+        _check(_lib.mlora_register_adapter_fused(self.handle, adapter_id, n, rows, ranks, pa, pb,
+                                                 _stream()), "mlora_register_adapter_fused")
         torch.cuda.current_stream().synchronize()
 
     def unregister(self, adapter_id: int):

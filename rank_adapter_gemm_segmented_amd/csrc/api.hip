@@ -259,6 +259,49 @@ int mlora_register_adapter(mlora_pool_t p, int adapter_id, int rank, const void*
   return MLORA_OK;
 }
 
+int mlora_register_adapter_fused(mlora_pool_t p, int adapter_id, int n_slices, const int* slice_rows,
+                                 const int* slice_ranks, const void* const* A, const void* const* B,
+                                 hipStream_t stream) {
+  if (!p || !slice_rows || !slice_ranks || !A || !B) return MLORA_ERR_INVALID_ARG;
+  if (n_slices < 1 || n_slices > MLORA_MAX_SLICES) return MLORA_ERR_SHAPE;
+  if (adapter_id < 0 || adapter_id >= p->capacity) return MLORA_ERR_ADAPTER;
+  if (p->host_rank[adapter_id] != 0) return MLORA_ERR_EXISTS;
+  long long rows = 0;
+  int rank = 0;
+  for (int m = 0; m < n_slices; ++m) {
+    if (!A[m] || !B[m]) return MLORA_ERR_INVALID_ARG;
+    if (slice_rows[m] < 1) return MLORA_ERR_SHAPE;
+    if (slice_ranks[m] < 1 || slice_ranks[m] > p->max_rank) return MLORA_ERR_RANK;
+    rows += slice_rows[m];
+    rank += slice_ranks[m];
+    if (rank > p->max_rank) return MLORA_ERR_RANK;
+  }
+  if (rows != p->d_out) return MLORA_ERR_SHAPE;
+  char* slot = (char*)p->base + (size_t)adapter_id * (size_t)p->slot_elems * p->elem;
+  char* bdst = slot + (size_t)p->b_offset * p->elem;
+  const int bld = (rank + 7) & ~7;
+  // B is block-diagonal: zero everywhere, then each slice's block
+  launch_fill_u32(bdst, (size_t)p->d_out * bld * p->elem / 4, 0u, stream);
+  if (check_launch() != MLORA_OK) return MLORA_ERR_HIP;
+  int r_off = 0, n_off = 0;
+  for (int m = 0; m < n_slices; ++m) {
+    const int r = slice_ranks[m];
+    hipError_t e = hipMemcpyAsync(slot + (size_t)r_off * p->d_in * p->elem, A[m],
+                                  (size_t)r * p->d_in * p->elem, hipMemcpyDefault, stream);
+    if (e != hipSuccess) return MLORA_ERR_HIP;
+    e = hipMemcpy2DAsync(bdst + ((size_t)n_off * bld + r_off) * p->elem, (size_t)bld * p->elem, B[m],
+                         (size_t)r * p->elem, (size_t)r * p->elem, (size_t)slice_rows[m],
+                         hipMemcpyDefault, stream);
+    if (e != hipSuccess) return MLORA_ERR_HIP;
+    r_off += r;
+    n_off += slice_rows[m];
+  }
+  launch_set_slot_rank(p->dev_rank, adapter_id, rank, stream);
+  if (check_launch() != MLORA_OK) return MLORA_ERR_HIP;
+  p->host_rank[adapter_id] = rank;
+  return MLORA_OK;
+}
+
 int mlora_unregister_adapter(mlora_pool_t p, int adapter_id, hipStream_t stream) {
   if (!p) return MLORA_ERR_INVALID_ARG;
   if (adapter_id < 0 || adapter_id >= p->capacity) return MLORA_ERR_ADAPTER;

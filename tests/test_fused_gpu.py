@@ -1,0 +1,116 @@
+"""GPU parity of fused multi-projection LoRA (``mlora_register_adapter_fused``).
+
+Several projections of one decoder layer (q|k|v, gate|up) are stacked into one
+base weight, and each adapter registers its per-projection (A_m, B_m) as one
+slot: A stacked, B block-diagonal. One ``mlora_linear`` call then serves every
+projection: one read of x, one shrink over the stacked A, and each projection's
+rows expand only their own part of v. An adapter's config names its target
+modules with one rank and one scaling ("Multi-LoRA Serving in Practice",
+section "1. Define Adapter Asset Standards").
+
+The oracle is the plain layer per projection, outputs side by side. Tolerance
+is the layer's bf16 bound, |y - y_ref| <= 2e-2 (1 + |y_ref|).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import BF16_TOL, compare, f32, i32, log, oracle_threads, sample_rows, to_dev, y_host
+from mlora_inputs import FUSED_WORKLOADS, make_fused_case
+
+pytestmark = pytest.mark.gpu
+
+
+class FusedDeviceCase:
+    """Stacked projections resident on the GPU with fused adapters registered."""
+
+    def __init__(self, slices):
+        import rank_adapter_gemm_segmented_amd as ml
+        self.ml = ml
+        self.slices = slices
+        c0 = slices[0]
+        n = len(slices)
+        self.d_out = sum(c.d_out for c in slices)
+        self.R = sum(c.max_rank for c in slices)
+        self.x = to_dev(c0.x, "bf16")
+        self.W = to_dev(np.vstack([c.W for c in slices]), "bf16")
+        self.pool = ml.Pool(c0.d_in, self.d_out, torch.bfloat16, self.R, c0.capacity)
+        for aid in sorted(c0.adapters):
+            self.pool.register_fused(aid, [(to_dev(c.adapters[aid].A, "bf16"), to_dev(c.adapters[aid].B, "bf16"))
+                                           for c in slices])
+        self.ws = self.pool.workspace(c0.n_tokens)
+        self.seg_start = i32(c0.seg_start)
+        self.seg_adapter = i32(c0.seg_adapter)
+        self.seg_rank = i32(np.where(c0.seg_adapter >= 0, c0.seg_rank * n, 0))
+        self.seg_scale = f32(c0.seg_scale)
+
+    def run(self, lora_on):
+        y = self.ml.linear(self.x, self.W, self.pool, self.seg_start, self.seg_adapter, self.seg_rank,
+                           self.seg_scale, lora_on=lora_on, workspace=self.ws)
+        torch.cuda.synchronize()
+        return y
+
+
+@pytest.mark.parametrize("name", sorted(FUSED_WORKLOADS))
+def test_fused_parity(name):
+    slices = make_fused_case(name)
+    c0 = slices[0]
+    log(f"[fused] {name}: T={c0.n_tokens}, d_out {[c.d_out for c in slices]}, rank {c0.max_rank} x {len(slices)}")
+    dc = FusedDeviceCase(slices)
+    # full rows up to the verify batch; prefill: every segment's first and last row plus random rows
+    rows = None if c0.n_tokens <= 256 else sample_rows(c0, 96, seed=5)
+    for lora_on in (1, 0):
+        y = y_host(dc.run(lora_on))
+        y_ref = oracle.fused_case_linear(slices, lora_on, rows=rows, threads=oracle_threads())
+        worst = compare(y if rows is None else y[rows], y_ref, BF16_TOL, f"{name} lora_on={lora_on}")
+        log(f"  lora_on={lora_on}: max err/bound {worst:.3f}")
+
+
+def test_fused_matches_separate_calls_in_lora_term():
+    # the fused call's adapter term per slice equals that of a separate call on
+    # the slice (both against LoRA-off of the same call, so the base product's
+    # summation order drops out); the difference of two bf16 outputs is
+    # bounded by their two roundings
+    name = "fused_qkv_decode"
+    slices = make_fused_case(name)
+    log(f"[fused] {name}: fused vs separate adapter terms")
+    import rank_adapter_gemm_segmented_amd as ml
+    dc = FusedDeviceCase(slices)
+    y_on = y_host(dc.run(1))
+    y_off = y_host(dc.run(0))
+    n0 = 0
+    for c in slices:
+        pool = ml.Pool(c.d_in, c.d_out, torch.bfloat16, c.max_rank, c.capacity)
+        for aid in sorted(c.adapters):
+            pool.register(aid, to_dev(c.adapters[aid].A, "bf16"), to_dev(c.adapters[aid].B, "bf16"))
+        W = to_dev(c.W, "bf16")
+        ys_on = ml.linear(dc.x, W, pool, i32(c.seg_start), i32(c.seg_adapter), i32(c.seg_rank),
+                          f32(c.seg_scale), lora_on=1)
+        ys_off = ml.linear(dc.x, W, pool, lora_on=0)
+        torch.cuda.synchronize()
+        d_fused = y_on[:, n0:n0 + c.d_out] - y_off[:, n0:n0 + c.d_out]
+        d_sep = y_host(ys_on) - y_host(ys_off)
+        mag = np.abs(y_on[:, n0:n0 + c.d_out]) + np.abs(y_off[:, n0:n0 + c.d_out])
+        assert np.all(np.abs(d_fused - d_sep) <= 1.5 * 2.0 ** -7 * mag + 1e-6), c.name
+        n0 += c.d_out
+
+
+def test_fused_registration_errors():
+    log("[fused] registration errors")
+    import rank_adapter_gemm_segmented_amd as ml
+    E = ml.STATUS_CODE
+    pool = ml.Pool(64, 48, torch.bfloat16, 16, 2)
+    A = torch.zeros(8, 64, dtype=torch.bfloat16, device="cuda")
+    B = torch.zeros(24, 8, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ml.MloraError) as e:       # rows 24 + 20 != 48
+        pool.register_fused(0, [(A, B), (A, B[:20])])
+    assert e.value.code == E["MLORA_ERR_SHAPE"]
+    with pytest.raises(ml.MloraError) as e:       # rank 8 + 8 + 8 > max_rank 16
+        pool.register_fused(0, [(A, B[:16]), (A, B[:16]), (A, B[:16])])
+    assert e.value.code == E["MLORA_ERR_RANK"]
+    pool.register_fused(1, [(A, B), (A, B)])
+    assert pool.rank(1) == 16
+    with pytest.raises(ml.MloraError) as e:
+        pool.register_fused(1, [(A, B), (A, B)])
+    assert e.value.code == E["MLORA_ERR_EXISTS"]

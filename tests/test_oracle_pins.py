@@ -333,10 +333,45 @@ def pin_merge_unmerge_and_linearity(lib):
     assert np.max(np.abs(back - W)) <= 2.0 ** -24 * np.max(np.abs(m1)) * 2
 
 
+def pin_fused_slices_are_block_diagonal(lib):
+    # projections stacked into one W with their adapters' A stacked and B
+    # block-diagonal give, through numpy fp64 products, the slices' outputs
+    # side by side (the packing a fused adapter registration relies on)
+    rng = np.random.default_rng(12)
+    d_in, rows, ranks = 24, [10, 6, 6], [3, 3, 3]
+    T = 9
+    ids = sorted(rng.integers(-1, 3, size=T).tolist())
+    scales = {a: float(rng.normal()) for a in range(3)}
+    slices = [make_custom_case(400 + m, "f32", d_in, rows[m], ids, {a: ranks[m] for a in range(3)},
+                               scales=scales) for m in range(3)]
+    x = slices[0].x
+    for c in slices[1:]:
+        c.x = x
+    y = np.concatenate([oracle.linear(c.x, c.W, _pool(c.adapters, c.capacity, d_in, c.d_out),
+                                      c.seg_start, c.seg_adapter, c.seg_rank, c.seg_scale, None, 1,
+                                      lib=lib) for c in slices], axis=1)
+    Wcat = np.vstack([c.W for c in slices]).astype(np.float64)
+    R = sum(ranks)
+    ref = x.astype(np.float64) @ Wcat.T
+    for t, a in enumerate(ids):
+        if a < 0:
+            continue
+        Acat = np.vstack([c.adapters[a].A for c in slices]).astype(np.float64)
+        Bbd = np.zeros((sum(rows), R))
+        n0 = r0 = 0
+        for m, c in enumerate(slices):
+            Bbd[n0:n0 + rows[m], r0:r0 + ranks[m]] = c.adapters[a].B
+            n0 += rows[m]
+            r0 += ranks[m]
+        ref[t] += np.float64(np.float32(scales[a])) * (Bbd @ (Acat @ x[t].astype(np.float64)))
+    assert _rel_err(y, ref) < 1e-12
+
+
 PINS = [pin_hand_example, pin_base_is_library_product, pin_lora_term_is_library_product,
         pin_merged_weights, pin_vanishing_terms, pin_one_hot_and_rank_one, pin_permutation,
         pin_linearity, pin_segmentation_exhaustive, pin_token_map, pin_merge_is_library_product,
-        pin_merge_serves_like_adapter, pin_merge_closed_forms, pin_merge_unmerge_and_linearity]
+        pin_merge_serves_like_adapter, pin_merge_closed_forms, pin_merge_unmerge_and_linearity,
+        pin_fused_slices_are_block_diagonal]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
