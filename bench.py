@@ -29,6 +29,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import re
 import os
 import sys
 import time
@@ -62,7 +63,7 @@ def parse():
     ap.add_argument("--workload", default="decode_bf16",
                     choices=["decode_bf16", "verify_bf16", "hetero_bf16", "prefill_bf16", "tiny_f32",
                              "merge_bf16", "fused_qkv_decode", "fused_gateup_verify",
-                             "fused_qkv_prefill", "fused_gateup_prefill"])
+                             "fused_qkv_prefill", "fused_gateup_prefill", "cycle_verify"])
     ap.add_argument("--proj", default="q", help="prefill projection (also the merge shape)")
     ap.add_argument("--rank", type=int, default=64, help="adapter rank of the merge workload")
     ap.add_argument("--rotate-gib", type=float, default=1.0)
@@ -108,7 +109,8 @@ def ingest_counters(workload: str, kernels, fetch_csv: str, write_csv: str) -> d
         factor = CALIB_BYTES / (calib * 1024.0)
         kib = {}
         for k in kernels:
-            hits = [v for n, v in vals.items() if f"mlora::{k}" in n or n.startswith(f"void mlora::{k}<")]
+            pat = re.compile(rf"::{k}[<(]")
+            hits = [v for n, v in vals.items() if pat.search(n)]
             if not hits:
                 raise SystemExit(f"{path}: kernel {k} not found")
             flat = [x for h in hits for x in h]
@@ -125,6 +127,16 @@ def ingest_counters(workload: str, kernels, fetch_csv: str, write_csv: str) -> d
         json.dump(allt, fh, indent=1, sort_keys=True)
         fh.write("\n")
     return out
+
+
+def counted_traffic(workload: str):
+    """HBM bytes per call from profiles/traffic.json, or None when the entry
+    is missing or was taken on other kernel sources."""
+    try:
+        ent = json.load(open(TRAFFIC_FILE)).get(workload, {})
+    except (ValueError, OSError):
+        return None
+    return ent.get("bytes_per_step") if ent.get("kernel_source_hash") == kernel_source_hash() else None
 
 
 def shrink_split(case) -> int:
@@ -170,6 +182,9 @@ def bench_merge(args):
     d_in, d_out = PREFILL_SHAPES[args.proj]
     r = args.rank
     name = f"merge_bf16_{args.proj}_r{r}"
+    if args.ingest_counters:
+        print(json.dumps({name: ingest_counters(name, ["k_merge_bf16"], *args.ingest_counters)}))
+        return
     torch.cuda.set_device(0)
     W, ad = make_merge_inputs(2000 + r, "bf16", d_in, d_out, r)
     W0 = to_dev(W, "bf16")
@@ -259,7 +274,8 @@ def bench_merge(args):
         "config": {"workload": name, "d_in": d_in, "d_out": d_out, "rank": r, "buffer_sets": n_sets,
                    "algorithmic_bytes": alg},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "algorithmic_bytes": alg,
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": counted_traffic(name),
+                     "algorithmic_bytes": alg,
                      "us_per_call": round(ms * 1e3, 3), "kernels": ["k_merge_bf16"],
                      "kernel_source_hash": kernel_source_hash()},
         "copy_reference": {"us_per_call": round(ms_copy * 1e3, 3),
@@ -379,6 +395,90 @@ def bench_fused(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_cycle(args):
+    """The InvisibleLoRA cycle at one gate/up layer (4096->14336, one rank-16
+    adapter per request, scale 2): LoRA-on and LoRA-off passes over b tokens
+    (one per request) and a LoRA-on pass over 2 b tokens (last committed token
+    + draft per request), for several batch sizes b, with the per-token
+    estimate and gate decision of rank_adapter_gemm_segmented_amd.cycle at the
+    pages' median acceptance rates."""
+    import numpy as np
+    import torch
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import rank_adapter_gemm_segmented_amd as ml
+    from rank_adapter_gemm_segmented_amd.cycle import break_even_alpha, cycle_estimate
+    from gpu_util import f32, i32, to_dev
+    from mlora_inputs import make_custom_case
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    b_max, d_in, d_out, r = 128, 4096, 14336, 16
+    case = make_custom_case(4000, "bf16", d_in, d_out, np.repeat(np.arange(b_max), 2),
+                            {a: r for a in range(b_max)}, scales={a: 2.0 for a in range(b_max)})
+    W0 = to_dev(case.W, "bf16")
+    x0 = to_dev(case.x, "bf16")
+    dev_ad = [(to_dev(case.adapters[a].A, "bf16"), to_dev(case.adapters[a].B, "bf16")) for a in range(b_max)]
+    set_bytes = W0.numel() * 2 + b_max * r * (d_in + d_out) * 2
+    n_sets = max(2, int(np.ceil(args.rotate_gib * (1 << 30) / set_bytes)))
+    sets = []
+    for i in range(n_sets):
+        pool = ml.Pool(d_in, d_out, torch.bfloat16, r, b_max)
+        for a, (A, B) in enumerate(dev_ad):
+            pool.register(a, A, B)
+        sets.append((W0 if i == 0 else W0.clone(), pool, pool.workspace(2 * b_max),
+                     torch.empty((2 * b_max, d_out), dtype=torch.bfloat16, device="cuda")))
+    torch.cuda.synchronize()
+
+    def meta(b, per_req):
+        return (i32(np.arange(b + 1) * per_req), i32(np.arange(b)), i32(np.full(b, r)), f32(np.full(b, 2.0)))
+
+    def timed(b, per_req, lora_on):
+        T = b * per_req
+        x = x0[:T]
+        m = meta(b, per_req)
+
+        def step(i):
+            W, pool, ws, y = sets[i % n_sets]
+            ml.linear(x, W, pool, *m, lora_on=lora_on, out=y[:T], workspace=ws)
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.steps):
+            step(i)
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) / args.steps * 1e3   # us per call
+
+    rows = []
+    for b in (16, 32, 64, 128):
+        t_on_b, t_off_b, t_on_2b = timed(b, 1, 1), timed(b, 1, 0), timed(b, 2, 1)
+        ent = {"requests": b, "t_on_b_us": round(t_on_b, 2), "t_off_b_us": round(t_off_b, 2),
+               "t_on_2b_us": round(t_on_2b, 2),
+               "break_even_alpha": round(break_even_alpha(t_on_b, t_off_b, t_on_2b), 4)}
+        for alpha in (0.92, 0.97):
+            est = cycle_estimate(t_on_b, t_off_b, t_on_2b, alpha)
+            ent[f"alpha_{alpha}"] = {"per_token_us": round(est.per_token_cycle, 2),
+                                    "speedup": round(est.speedup, 4), "draft": est.draft}
+        rows.append(ent)
+        print(f"[bench] cycle b={b}: on {t_on_b:.1f} off {t_off_b:.1f} on(2b) {t_on_2b:.1f} us, "
+              f"break-even alpha {ent['break_even_alpha']:.3f}", file=sys.stderr, flush=True)
+    last = rows[-1]
+    out = {
+        "metric": "InvisibleLoRA cycle at one layer: time per committed token, drafting vs plain LoRA-on decoding",
+        "value": last["alpha_0.97"]["speedup"], "unit": "x (plain / cycle, alpha 0.97, 128 requests)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian weights, adapters and activations)",
+        "config": {"workload": "cycle_verify", "d_in": d_in, "d_out": d_out, "rank": r,
+                   "adapters": "one per request", "buffer_sets": n_sets},
+        "batches": rows,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -391,6 +491,9 @@ def main():
         return
     if args.workload.startswith("fused_"):
         bench_fused(args)
+        return
+    if args.workload == "cycle_verify":
+        bench_cycle(args)
         return
 
     import numpy as np
@@ -492,16 +595,8 @@ def main():
     tf_off = flops_off / (ms_off * 1e-3) / 1e12
 
     # ---- HBM traffic from committed counter runs (only if sources match) ----
-    traffic = None
+    traffic = counted_traffic(case.name)
     src_hash = kernel_source_hash()
-    if os.path.exists(TRAFFIC_FILE):
-        try:
-            tr = json.load(open(TRAFFIC_FILE))
-            ent = tr.get(case.name, {})
-            if ent.get("kernel_source_hash") == src_hash:
-                traffic = ent.get("bytes_per_step")
-        except (ValueError, OSError):
-            traffic = None
 
     kernels = layer_kernels(case)
     roofline = {"bound": "hbm", "achieved": round(gbs_on, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

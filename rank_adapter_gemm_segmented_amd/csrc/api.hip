@@ -319,7 +319,11 @@ int mlora_adapter_rank(mlora_pool_t p, int adapter_id) {
 
 size_t mlora_workspace_bytes(mlora_pool_t p, int max_tokens) {
   if (!p || max_tokens < 0 || max_tokens > MLORA_MAX_TOKENS) return 0;
-  return ws_layout(p, max_tokens).total;
+  // the layout grows with T within T <= 64 (decode partial tiles) and within
+  // T > 64, but a batch of <= 64 tokens may need more than a larger one
+  const size_t big = ws_layout(p, max_tokens).total;
+  const size_t small = ws_layout(p, max_tokens < 64 ? max_tokens : 64).total;
+  return big > small ? big : small;
 }
 
 int mlora_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream) {

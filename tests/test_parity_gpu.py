@@ -219,3 +219,26 @@ def test_mid_size_batches(T):
     dc = DeviceCase(c)
     check_case(dc, 1, sample_rows(c, 48), what=f"mid-size T={T} lora_on=1")
     check_case(dc, 0, sample_rows(c, 16, seed=1), what=f"mid-size T={T} lora_on=0")
+
+
+@pytest.mark.gpu
+def test_workspace_for_max_tokens_serves_smaller_batches():
+    # mlora_workspace_bytes(pool, N) covers every call of up to N tokens: a
+    # workspace sized for a 256-token batch also serves decode batches
+    # (T <= 64), whose split-K partial tiles larger batches do not use
+    log("[parity] one workspace for batches of 16, 64 and 256 tokens")
+    import rank_adapter_gemm_segmented_amd as ml
+    ids = sorted(np.random.default_rng(7).integers(0, 8, size=256).tolist())
+    c = make_custom_case(95, "bf16", 1024, 1536, ids, {a: 16 for a in range(8)})
+    dc = DeviceCase(c)
+    ws = dc.pool.workspace(256)
+    assert ws.numel() >= dc.pool.workspace_bytes(16) and ws.numel() >= dc.pool.workspace_bytes(64)
+    for T in (16, 64, 256):
+        # the first T rows of the batch, with their own segments
+        sub = make_custom_case(95, "bf16", 1024, 1536, ids[:T], {a: 16 for a in range(8)})
+        sub.W, sub.adapters, sub.x = c.W, c.adapters, c.x[:T]
+        y = ml.linear(dc.x[:T], dc.W, dc.pool, i32(sub.seg_start), i32(sub.seg_adapter),
+                      i32(sub.seg_rank), f32(sub.seg_scale), lora_on=1, workspace=ws)
+        torch.cuda.synchronize()
+        compare(y_host(y), oracle.case_linear(sub, 1, threads=oracle_threads()), 2e-2,
+                f"shared workspace T={T}")
