@@ -157,10 +157,12 @@ def shrink_split(case) -> int:
 
 def layer_kernels(case):
     """Kernels of one LoRA-on layer call, run back to back on one stream: the
-    split-K stream + finish pair for T <= 64 in bf16; above that segment build
+    split-K stream + finish pair for T <= 64 in bf16 (T < 48 on layers of
+    8192 outputs or more); above that segment build
     (unsorted input), the shrink, the v fold (only when the shrink splits d_in)
     and the tiled GEMM with fused expand; shrink + GEMM for fp32."""
-    if case.dtype == "bf16" and case.n_tokens <= 64:
+    wide = case.n_tokens >= 48 and case.d_out >= 8192    # api.hip sends these to the GEMM
+    if case.dtype == "bf16" and case.n_tokens <= 64 and not wide:
         return ["k_stream_bf16", "k_finish_bf16"]
     if case.dtype == "bf16":
         return ((["k_build_segments"] if not case.sorted_input else []) + ["k_shrink2"] +

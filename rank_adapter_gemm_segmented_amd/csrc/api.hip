@@ -131,8 +131,12 @@ int run_linear(const void* x, const void* W, mlora_pool_s* pool, const SegView& 
   a.seg_grid = lora_on ? sv.n_seg : 0;
   if (pool->dtype == MLORA_BF16) {
     const int fp = forced_path();
+    // the split-K decode path up to 64 tokens, except on wide layers from 48
+    // tokens up, where the tiled GEMM measured faster (4096 -> 14336 at 48 and
+    // 64 tokens: LoRA-off 31 vs 44 us, LoRA-on equal)
+    const bool wide = T >= 48 && pool->d_out >= 8192;
     const bool dec_ok = decode_supported(T, lora_on ? sv.n_seg : 0, pool->d_out, pool->max_rank);
-    if (dec_ok && fp != 2) {
+    if (dec_ok && (fp == 1 || (fp == 0 && !wide))) {
       DecodeArgs d;
       d.x = x;
       d.W = W;

@@ -242,3 +242,16 @@ def test_workspace_for_max_tokens_serves_smaller_batches():
         torch.cuda.synchronize()
         compare(y_host(y), oracle.case_linear(sub, 1, threads=oracle_threads()), 2e-2,
                 f"shared workspace T={T}")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("T", [47, 48, 64])
+def test_wide_layer_path_switch(T):
+    # 48..64 tokens on a layer of >= 8192 outputs take the tiled GEMM path by
+    # default, 47 tokens the split-K decode path; both match the oracle
+    log(f"[parity] wide layer, default path, T={T}: 512->8200")
+    ids = sorted(np.random.default_rng(300 + T).integers(-1, 20, size=T).tolist())
+    c = make_custom_case(300 + T, "bf16", 512, 8200, ids, {a: [16, 8, 32][a % 3] for a in range(20)})
+    dc = DeviceCase(c)
+    check_case(dc, 1, what=f"wide T={T} lora_on=1")
+    check_case(dc, 0, what=f"wide T={T} lora_on=0")
