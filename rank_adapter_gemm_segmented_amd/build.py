@@ -18,7 +18,7 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["api.hip", "kernels_meta.hip", "kernels_gemm.hip", "kernels_decode.hip", "kernels_f32.hip",
-           "kernels_merge.hip"]
+           "kernels_merge.hip", "kernels_gemv.hip"]
 
 # Packed fp32 VALU ops are disabled for every device compile.
 FLAGS = [

@@ -105,7 +105,8 @@ int hip_status(hipError_t e) { return e == hipSuccess ? MLORA_OK : MLORA_ERR_HIP
 // measurements); unset or anything else chooses by token count.
 int forced_path() {
   const char* e = getenv("MLORA_FORCE_PATH");
-  return (e && !strcmp(e, "decode")) ? 1 : (e && !strcmp(e, "gemm")) ? 2 : 0;
+  if (!e) return 0;
+  return !strcmp(e, "decode") ? 1 : !strcmp(e, "gemm") ? 2 : !strcmp(e, "gemv") ? 3 : 0;
 }
 
 int check_launch() { return hip_status(hipGetLastError()); }
@@ -161,6 +162,11 @@ int run_linear(const void* x, const void* W, mlora_pool_s* pool, const SegView& 
     // faster there; longer or higher-rank segments gain from the split)
     const bool one_chunk = lora_on && T <= 16 * a.seg_grid && pool->max_rank <= 16;
     a.ks = one_chunk ? 1 : choose_shrink_split_bf16(pool->d_in, shrink_items_bound(T, a.seg_grid));
+    if (fp == 3 && T <= 64) {
+      launch_shrink_bf16(a, stream);
+      launch_gemv_bf16(a, stream);
+      return check_launch();
+    }
     launch_linear_bf16(a, stream);
   } else {
     a.ks = 1;

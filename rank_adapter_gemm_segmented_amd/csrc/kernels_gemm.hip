@@ -795,7 +795,7 @@ static void launch_g(const LinearArgs& a, hipStream_t st) {
 // Tile choice: large batches take 256x256 tiles (MFMA-bound, ~30 B/clk of L2
 // per CU); otherwise a tile spans every position of the batch (one read of x
 // per CU) with as few W rows as keep the CUs busy.
-void launch_linear_bf16(const LinearArgs& a, hipStream_t st) {
+void launch_shrink_bf16(const LinearArgs& a, hipStream_t st) {
   if (a.lora_on && a.seg_grid > 0) {
     // block counts of the shrink: ranks up to the pool's (at most 64 per
     // pass) and 16 or 64 positions per pass, by the batch's mean segment length
@@ -818,6 +818,10 @@ void launch_linear_bf16(const LinearArgs& a, hipStream_t st) {
       hipLaunchKernelGGL(k_vfinal, dim3((n4 + 255) / 256), dim3(256), 0, st, a);
     }
   }
+}
+
+void launch_linear_bf16(const LinearArgs& a, hipStream_t st) {
+  launch_shrink_bf16(a, st);
   auto tiles = [&](int br, int bt) {
     return (long long)((a.d_out + br - 1) / br) * ((a.T + bt - 1) / bt);
   };

@@ -78,8 +78,14 @@ void launch_validate(const int32_t* seg_start, const int32_t* seg_adapter, const
 void launch_fill_u32(void* p, size_t n_words, uint32_t v, hipStream_t st);
 void launch_set_slot_rank(int32_t* table, int id, int rank, hipStream_t st);
 
-// bf16 path for larger token counts (kernels_gemm.hip)
+// bf16 path for larger token counts (kernels_gemm.hip); the shrink alone
+// (k_shrink2, and k_vfinal when ks > 1) writes pos_info and v_fin
 void launch_linear_bf16(const LinearArgs& a, hipStream_t st);
+void launch_shrink_bf16(const LinearArgs& a, hipStream_t st);
+
+// full-d_in GEMV with the expand for T <= 64 (kernels_gemv.hip); LoRA-on
+// needs launch_shrink_bf16 first
+void launch_gemv_bf16(const LinearArgs& a, hipStream_t st);
 int choose_shrink_split_bf16(int d_in, int seg_grid);
 int shrink_items_bound(int T, int n_seg_bound);
 

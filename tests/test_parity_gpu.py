@@ -193,7 +193,7 @@ _FORCED_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("path", ["decode", "gemm"])
+@pytest.mark.parametrize("path", ["decode", "gemm", "gemv"])
 @pytest.mark.parametrize("idx", range(len(_FORCED_SHAPES)))
 def test_forced_paths(path, idx, monkeypatch):
     seed, d_in, d_out, ids, r = _FORCED_SHAPES[idx]
