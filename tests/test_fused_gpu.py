@@ -114,3 +114,39 @@ def test_fused_registration_errors():
     with pytest.raises(ml.MloraError) as e:
         pool.register_fused(1, [(A, B), (A, B)])
     assert e.value.code == E["MLORA_ERR_EXISTS"]
+
+
+def test_fused_unsorted_batch():
+    # the unsorted entry point segments the batch itself and takes each
+    # segment's rank from the slot (the stacked rank of the fused adapter)
+    name = "fused_qkv_decode"
+    slices = make_fused_case(name)
+    c0 = slices[0]
+    log(f"[fused] {name} through mlora_linear_tokens, rows shuffled")
+    dc = FusedDeviceCase(slices)
+    perm = np.random.default_rng(3).permutation(c0.n_tokens)
+    tok = c0.token_adapter[perm]
+    xp = dc.x[torch.from_numpy(perm).cuda()].contiguous()
+    y = dc.ml.linear_tokens(xp, dc.W, dc.pool, i32(tok), f32(c0.adapter_scale), lora_on=1, workspace=dc.ws)
+    torch.cuda.synchronize()
+    y_ref = oracle.fused_case_linear(slices, 1, threads=oracle_threads())[perm]
+    worst = compare(y_host(y), y_ref, BF16_TOL, f"{name} unsorted")
+    log(f"  max err/bound {worst:.3f}")
+
+
+def test_fused_merge_equals_per_projection_merges():
+    # merging a fused adapter into the stacked W merges every projection with
+    # its own A_m, B_m: the zero blocks of B add exactly nothing
+    import rank_adapter_gemm_segmented_amd as ml
+    slices = make_fused_case("fused_qkv_decode")
+    log("[fused] merge of a fused adapter vs per-projection merges")
+    dc = FusedDeviceCase(slices)
+    Wm = y_host(ml.merge_adapter(dc.W, dc.pool, 5, 2.0))
+    n0 = 0
+    for c in slices:
+        pool = ml.Pool(c.d_in, c.d_out, torch.bfloat16, c.max_rank, c.capacity)
+        pool.register(5, to_dev(c.adapters[5].A, "bf16"), to_dev(c.adapters[5].B, "bf16"))
+        ref = y_host(ml.merge_adapter(to_dev(c.W, "bf16"), pool, 5, 2.0))
+        torch.cuda.synchronize()
+        assert np.array_equal(Wm[n0:n0 + c.d_out], ref), c.name
+        n0 += c.d_out
