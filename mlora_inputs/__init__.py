@@ -43,6 +43,7 @@ __all__ = [
     "Adapter", "Case", "bf16_round", "bf16_bits", "bf16_from_bits",
     "make_case", "make_custom_case", "WORKLOADS", "PREFILL_SHAPES",
     "sorted_metadata", "zipf_probs", "make_merge_inputs", "make_fused_case", "FUSED_WORKLOADS",
+    "e4m3_quantize_rows", "make_fp8w_case",
 ]
 
 
@@ -350,3 +351,26 @@ def make_fused_case(name: str) -> List[Case]:
                           d_in, d_out, 0.02, 0.01, base.dtype)
         cases.append(dataclasses.replace(base, name=f"{name}_{proj}", d_out=d_out, W=W, adapters=pool))
     return cases
+
+
+def e4m3_quantize_rows(W: np.ndarray):
+    """A base weight stored as FP8: per output row a float32 scale
+    s = max|W_row| / 448 (448 is the largest e4m3 value) and e4m3 codes of
+    W_row / s, rounded to nearest even by torch's float8_e4m3fn cast. Returns
+    (codes uint8 [d_out, d_in], scale float32 [d_out]). Rows of zeros get
+    scale 1."""
+    import torch
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    amax = np.max(np.abs(W), axis=1)
+    scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    q = torch.from_numpy(W / scale[:, None]).to(torch.float8_e4m3fn)
+    return q.view(torch.uint8).numpy().copy(), scale
+
+
+def make_fp8w_case(name: str = "decode_bf16", proj: str = "q"):
+    """A workload whose base weight is stored as FP8 (e4m3 codes plus a
+    float32 scale per output row, from the workload's own W); x, adapters and
+    segments are the workload's, in bf16. Returns (case, codes, scale)."""
+    case = make_case(name, proj)
+    codes, scale = e4m3_quantize_rows(case.W)
+    return case, codes, scale

@@ -223,3 +223,32 @@ def fused_case_linear(slice_cases, lora_on: int = 1, rows=None, threads: int = 0
     side in the order given."""
     return np.concatenate([case_linear(c, lora_on, rows=rows, threads=threads) for c in slice_cases],
                           axis=1)
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Values of FP8 e4m3 codes (OCP 8-bit floating point, E4M3: sign bit,
+    4 exponent bits with bias 7, 3 mantissa bits, no infinities; exponent 0 is
+    subnormal, m/8 * 2^-6; code S.1111.111 is NaN), as float32 (exact)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e - 7))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return (sign * mag).astype(np.float32)
+
+
+def fp8w_case_linear(case, codes, w_scale, lora_on: int = 1, rows=None, threads: int = 0):
+    """Oracle output of the layer whose base weight is stored as FP8: the
+    dequantized weight W[n, k] = w_scale[n] * e4m3(codes[n, k]), i.e.
+        y_i = diag(w_scale) (Q x_i) + scale_s B_a (A_a x_i)
+    with Q the decoded codes (the row scale taken out of the sum over k)."""
+    import dataclasses
+    Q = e4m3_decode(codes)
+    qcase = dataclasses.replace(case, W=Q)
+    base = case_linear(qcase, 0, rows=rows, threads=threads)
+    y = base * np.asarray(w_scale, np.float64)[None, :]
+    if lora_on:
+        zcase = dataclasses.replace(case, W=np.zeros_like(Q))
+        y = y + case_linear(zcase, 1, rows=rows, threads=threads)
+    return y

@@ -367,11 +367,44 @@ def pin_fused_slices_are_block_diagonal(lib):
     assert _rel_err(y, ref) < 1e-12
 
 
+def pin_e4m3_decoder_matches_torch(lib):
+    # every e4m3 code but the two NaNs, against torch's float8_e4m3fn
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    ours = oracle.e4m3_decode(codes)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).float().numpy()
+    finite = ~np.isnan(ref)
+    assert int(np.sum(~finite)) == 2 and np.all(np.isnan(ours[~finite]))
+    assert np.array_equal(ours[finite], ref[finite])
+    assert ours[0x7E] == 448.0 and ours[0x01] == 2.0 ** -9 and ours[0x08] == 2.0 ** -6
+
+
+def pin_fp8w_layer_is_library_product(lib):
+    # the FP8-weight layer: numpy fp64 products of the dequantized weight plus
+    # the adapter term
+    rng = np.random.default_rng(13)
+    T, d_in, d_out = 6, 48, 20
+    ids = sorted(rng.integers(-1, 3, size=T).tolist())
+    c = make_custom_case(500, "f32", d_in, d_out, ids, {0: 4, 1: 2, 2: 8}, scales={0: 1.5, 1: -2.0, 2: 0.5})
+    codes = rng.integers(0, 256, size=(d_out, d_in)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x38          # no NaN codes
+    w_scale = rng.uniform(0.5, 2.0, d_out).astype(np.float32)
+    y = oracle.fp8w_case_linear(c, codes, w_scale, 1)
+    Wd = w_scale[:, None].astype(np.float64) * oracle.e4m3_decode(codes).astype(np.float64)
+    ref = c.x.astype(np.float64) @ Wd.T
+    for t, a in enumerate(ids):
+        if a >= 0:
+            ad = c.adapters[a]
+            ref[t] += np.float64(c.adapter_scale[a]) * (ad.B.astype(np.float64) @ (ad.A.astype(np.float64) @ c.x[t].astype(np.float64)))
+    assert _rel_err(y, ref) < 1e-12
+
+
 PINS = [pin_hand_example, pin_base_is_library_product, pin_lora_term_is_library_product,
         pin_merged_weights, pin_vanishing_terms, pin_one_hot_and_rank_one, pin_permutation,
         pin_linearity, pin_segmentation_exhaustive, pin_token_map, pin_merge_is_library_product,
         pin_merge_serves_like_adapter, pin_merge_closed_forms, pin_merge_unmerge_and_linearity,
-        pin_fused_slices_are_block_diagonal]
+        pin_fused_slices_are_block_diagonal, pin_e4m3_decoder_matches_torch,
+        pin_fp8w_layer_is_library_product]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
