@@ -63,7 +63,7 @@ def parse():
     ap.add_argument("--workload", default="decode_bf16",
                     choices=["decode_bf16", "verify_bf16", "hetero_bf16", "prefill_bf16", "tiny_f32",
                              "merge_bf16", "fused_qkv_decode", "fused_gateup_verify",
-                             "fused_qkv_prefill", "fused_gateup_prefill", "cycle_verify"])
+                             "fused_qkv_prefill", "fused_gateup_prefill", "cycle_verify", "decode_fp8w"])
     ap.add_argument("--proj", default="q", help="prefill projection (also the merge shape)")
     ap.add_argument("--rank", type=int, default=64, help="adapter rank of the merge workload")
     ap.add_argument("--rotate-gib", type=float, default=1.0)
@@ -481,6 +481,102 @@ def bench_cycle(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_fp8w(args):
+    """The decode batch with the base weight stored as FP8 e4m3 (per-row
+    float32 scales) and bf16 adapters, LoRA-on and LoRA-off, over rotating
+    buffer sets. Algorithmic bytes: W codes + row scales + touched adapters'
+    A and B + x + y."""
+    import numpy as np
+    import torch
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import rank_adapter_gemm_segmented_amd as ml
+    from gpu_util import f32, i32, to_dev
+    from mlora_inputs import make_fp8w_case
+
+    case, codes, wsc = make_fp8w_case("decode_bf16")
+    T, d_in, d_out = case.n_tokens, case.d_in, case.d_out
+    touched = case.touched_adapters()
+    lora_bytes = sum((case.adapters[a].rank * d_in + d_out * case.adapters[a].rank) * 2 for a in touched)
+    base_bytes = d_out * d_in + d_out * 4 + (T * d_in + T * d_out) * 2
+    bytes_on, bytes_off = base_bytes + lora_bytes, base_bytes
+    if args.ingest_counters:
+        print(json.dumps({"decode_fp8w": ingest_counters("decode_fp8w", ["k_stream_bf16", "k_finish_bf16"],
+                                                          *args.ingest_counters)}))
+        return
+    torch.cuda.set_device(0)
+    W80 = torch.from_numpy(codes).cuda()
+    s0 = f32(wsc)
+    x0 = to_dev(case.x, "bf16")
+    pool0 = ml.Pool(d_in, d_out, torch.bfloat16, case.max_rank, case.capacity)
+    for aid in sorted(case.adapters):
+        ad = case.adapters[aid]
+        pool0.register(aid, to_dev(ad.A, "bf16"), to_dev(ad.B, "bf16"))
+    set_bytes = W80.numel() + pool0.arena.numel()
+    n_sets = 2 if args.profile else max(2, int(np.ceil(args.rotate_gib * (1 << 30) / set_bytes)))
+    sets = []
+    for i in range(n_sets):
+        if i == 0:
+            W8, pool = W80, pool0
+        else:
+            W8 = W80.clone()
+            pool = ml.Pool(d_in, d_out, torch.bfloat16, case.max_rank, case.capacity)
+            pool.arena.copy_(pool0.arena)
+        sets.append((W8, s0.clone(), pool, torch.empty((T, d_out), dtype=torch.bfloat16, device="cuda"),
+                     pool.workspace(T)))
+    meta = (i32(case.seg_start), i32(case.seg_adapter), i32(case.seg_rank), f32(case.seg_scale))
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def timed(lora_on, steps, warmup):
+        def step(i):
+            W8, sc, pool, y, ws = sets[i % n_sets]
+            ml.linear_fp8w(x0, W8, sc, pool, *meta, lora_on=lora_on, out=y, workspace=ws)
+        for i in range(warmup):
+            step(i)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps):
+            step(i)
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    if args.profile:
+        timed(1, 5, 2)
+        print("[bench] decode_fp8w: 7 lora_on calls done", file=sys.stderr, flush=True)
+        n = 256 << 20
+        src = torch.ones(n // 2, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] calibration copy of {n} bytes done", file=sys.stderr, flush=True)
+        return
+    ms_on = timed(1, args.steps, args.warmup)
+    ms_off = timed(0, args.steps, args.warmup)
+    print(f"[bench] decode_fp8w: lora_on {ms_on * 1e3:.2f} us/step, lora_off {ms_off * 1e3:.2f} us/step, "
+          f"{n_sets} buffer sets", file=sys.stderr, flush=True)
+    gbs_on = bytes_on / (ms_on * 1e-3) / 1e9
+    out = {
+        "metric": "multi-LoRA linear with an FP8 base weight, eff. HBM GB/s (% roofline); LoRA-on vs LoRA-off",
+        "value": round(gbs_on, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_on, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8 e4m3 W, bf16 x/adapters/y, fp32 accumulate",
+        "data": "synthetic (seeded Gaussian weights, adapters and activations; W quantized per row)",
+        "config": {"workload": "decode_fp8w", "tokens": T, "d_in": d_in, "d_out": d_out,
+                   "adapters_touched": len(touched), "buffer_sets": n_sets,
+                   "unique_bytes_lora_on": bytes_on, "unique_bytes_lora_off": bytes_off},
+        "lora_off": {"ms_per_step": round(ms_off, 6), "gbs": round(bytes_off / (ms_off * 1e-3) / 1e9, 1)},
+        "lora_on_overhead": round(ms_on / ms_off - 1.0, 4),
+        "roofline": {"bound": "hbm", "achieved": round(gbs_on, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs_on / HBM_PEAK_GBS, 4), "traffic": counted_traffic("decode_fp8w"),
+                     "algorithmic_bytes": bytes_on, "us_per_call": round(ms_on * 1e3, 3),
+                     "kernels": ["k_stream_bf16", "k_finish_bf16"], "kernel_source_hash": kernel_source_hash()},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -496,6 +592,9 @@ def main():
         return
     if args.workload == "cycle_verify":
         bench_cycle(args)
+        return
+    if args.workload == "decode_fp8w":
+        bench_fp8w(args)
         return
 
     import numpy as np

@@ -178,6 +178,31 @@ int mlora_linear(const void* x, const void* W, mlora_pool_t pool, const int32_t*
                  const int32_t* token_index, int n_tokens, int n_seg, int lora_on, void* y,
                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* The layer with the base weight stored as FP8 and the adapters in bf16:
+ *
+ *     y_i = diag(w_scale) (Q x_i) + scale_s * B_a (A_a x_i),
+ *
+ * i.e. the dequantized weight W[n, k] = w_scale[n] * e4m3(W_fp8[n, k]).
+ * Quantizing the weights of a LoRA-served model to FP8 is named by the "LoRA
+ * Inference" glossary (the paragraph on inference optimizations for merged
+ * weights); at decode the layer streams W from HBM, so one byte per weight
+ * halves the dominant traffic. W_fp8 [d_out, d_in] holds OCP FP8 E4M3 codes
+ * (bias 7, subnormals, no infinities; NaN codes are not supported), w_scale
+ * [d_out] float32 (device). x, y and the pool are bf16; each e4m3 value is
+ * exact in bf16, products accumulate in fp32, the row scale multiplies the
+ * finished base sum, and y is rounded to bf16 once. Other arguments as
+ * mlora_linear. Batches of 1 .. MLORA_MAX_FP8W_TOKENS tokens (the split-K
+ * decode path) and d_in a multiple of 16.
+ * Errors: as mlora_linear, plus MLORA_ERR_DTYPE (pool not bf16) and
+ * MLORA_ERR_SHAPE (more tokens, more segments or ranks than the decode path
+ * takes, or d_in not a multiple of 16). */
+#define MLORA_MAX_FP8W_TOKENS 64
+int mlora_linear_fp8w(const void* x, const uint8_t* W_fp8, const float* w_scale, mlora_pool_t pool,
+                      const int32_t* seg_start, const int32_t* seg_adapter, const int32_t* seg_rank,
+                      const float* seg_scale, const int32_t* token_index, int n_tokens, int n_seg,
+                      int lora_on, void* y, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
 /* Canonical segmentation of an unsorted batch on the device: tokens grouped
  * by adapter id in ascending id order (-1 first), tokens of one id in
  * ascending batch order. Outputs (device):

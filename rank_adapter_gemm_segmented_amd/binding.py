@@ -57,6 +57,7 @@ def _load() -> ctypes.CDLL:
         "mlora_validate": ([P, P, P, P, P, I, I, P, SZ, P], I),
         "mlora_merge_adapter": ([P, P, P, I, ctypes.c_float, P], I),
         "mlora_register_adapter_fused": ([P, I, I, P, P, P, P, P], I),
+        "mlora_linear_fp8w": ([P, P, P, P, P, P, P, P, P, I, I, I, P, P, SZ, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -200,6 +201,30 @@ def linear(x, W, pool: Pool, seg_start=None, seg_adapter=None, seg_rank=None, se
                              _ptr(seg_scale), _ptr(_i32(token_index, "token_index")), T, n_seg,
                              int(lora_on), _ptr(y), _ptr(ws), ws.numel(), _stream()),
            "mlora_linear")
+    return y
+
+
+def linear_fp8w(x, W_fp8, w_scale, pool: Pool, seg_start=None, seg_adapter=None, seg_rank=None,
+                seg_scale=None, lora_on: int = 1, token_index=None, out=None, workspace=None):
+    """``mlora_linear_fp8w``: the layer with an FP8 (e4m3 codes, uint8 [d_out, d_in])
+    base weight and float32 per-row scales; x, y and the pool in bf16."""
+    if x.dtype != torch.bfloat16 or pool.dtype != torch.bfloat16:
+        raise TypeError("x and the pool must be bf16")
+    if W_fp8.dtype != torch.uint8 or tuple(W_fp8.shape) != (pool.d_out, pool.d_in) or not W_fp8.is_contiguous():
+        raise ValueError("W_fp8 must be contiguous uint8 [d_out, d_in]")
+    if w_scale.dtype != torch.float32 or w_scale.numel() != pool.d_out or not w_scale.is_contiguous():
+        raise ValueError("w_scale must be contiguous float32 [d_out]")
+    if x.dim() != 2 or x.shape[1] != pool.d_in or not x.is_contiguous():
+        raise ValueError("x must be contiguous [T, d_in]")
+    T = int(x.shape[0])
+    y = out if out is not None else torch.empty((T, pool.d_out), dtype=pool.dtype, device=x.device)
+    ws = workspace if workspace is not None else pool.workspace(T)
+    n_seg = int(seg_adapter.numel()) if seg_adapter is not None else 0
+    _check(_lib.mlora_linear_fp8w(_ptr(x), _ptr(W_fp8), _ptr(w_scale), pool.handle,
+                                  _ptr(_i32(seg_start, "seg_start")), _ptr(_i32(seg_adapter, "seg_adapter")),
+                                  _ptr(_i32(seg_rank, "seg_rank")), _ptr(seg_scale),
+                                  _ptr(_i32(token_index, "token_index")), T, n_seg, int(lora_on), _ptr(y),
+                                  _ptr(ws), ws.numel(), _stream()), "mlora_linear_fp8w")
     return y
 
 

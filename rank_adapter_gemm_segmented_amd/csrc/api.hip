@@ -112,8 +112,10 @@ int forced_path() {
 int check_launch() { return hip_status(hipGetLastError()); }
 
 // Launch the layer on sorted metadata already resident on the device.
+// w_scale != null: W holds FP8 e4m3 codes with a float32 scale per row (bf16
+// pool, split-K decode path only; the caller has checked the shape).
 int run_linear(const void* x, const void* W, mlora_pool_s* pool, const SegView& sv, int T,
-               int lora_on, void* y, char* ws, hipStream_t stream) {
+               int lora_on, void* y, char* ws, hipStream_t stream, const float* w_scale = nullptr) {
   const WsLayout L = ws_layout(pool, T);
   LinearArgs a;
   a.x = x;
@@ -137,7 +139,7 @@ int run_linear(const void* x, const void* W, mlora_pool_s* pool, const SegView& 
     // 64 tokens: LoRA-off 31 vs 44 us, LoRA-on equal)
     const bool wide = T >= 48 && pool->d_out >= 8192;
     const bool dec_ok = decode_supported(T, lora_on ? sv.n_seg : 0, pool->d_out, pool->max_rank);
-    if (dec_ok && (fp == 1 || (fp == 0 && !wide))) {
+    if (w_scale || (dec_ok && (fp == 1 || (fp == 0 && !wide)))) {
       DecodeArgs d;
       d.x = x;
       d.W = W;
@@ -154,6 +156,7 @@ int run_linear(const void* x, const void* W, mlora_pool_s* pool, const SegView& 
       d.r_ws = a.r_ws;
       decode_plan(pool->d_in, pool->d_out, &d.n_tiles, &d.kc, &d.n_chunks);
       d.unit_rows = decode_unit_rows(lora_on ? sv.n_seg : 0, pool->max_rank, d.n_tiles);
+      d.w_scale = w_scale;
       launch_decode_bf16(d, stream);
       return check_launch();
     }
@@ -368,6 +371,39 @@ int mlora_linear(const void* x, const void* W, mlora_pool_t pool, const int32_t*
     sv.n_seg = n_seg;
   }
   return run_linear(x, W, pool, sv, n_tokens, lora_on, y, (char*)workspace, stream);
+}
+
+int mlora_linear_fp8w(const void* x, const uint8_t* W_fp8, const float* w_scale, mlora_pool_t pool,
+                      const int32_t* seg_start, const int32_t* seg_adapter, const int32_t* seg_rank,
+                      const float* seg_scale, const int32_t* token_index, int n_tokens, int n_seg,
+                      int lora_on, void* y, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  if (!pool) return MLORA_ERR_INVALID_ARG;
+  if (pool->dtype != MLORA_BF16) return MLORA_ERR_DTYPE;
+  if (lora_on != 0 && lora_on != 1) return MLORA_ERR_INVALID_ARG;
+  if (n_tokens < 0 || n_tokens > MLORA_MAX_FP8W_TOKENS) return MLORA_ERR_SHAPE;
+  if (pool->d_in % 16 != 0) return MLORA_ERR_SHAPE;
+  if (n_tokens == 0) return MLORA_OK;
+  if (!x || !W_fp8 || !w_scale || !y || !workspace) return MLORA_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(W_fp8) || !aligned16(y) || !aligned16(workspace))
+    return MLORA_ERR_INVALID_ARG;
+  if (workspace_bytes < ws_layout(pool, n_tokens).total) return MLORA_ERR_WORKSPACE;
+  SegView sv{};
+  if (lora_on) {
+    if (!seg_start || !seg_adapter || !seg_rank || !seg_scale) return MLORA_ERR_INVALID_ARG;
+    if (n_seg < 1) return MLORA_ERR_METADATA;
+    if (n_seg > MLORA_MAX_SEGMENTS) return MLORA_ERR_SHAPE;
+    sv.seg_start = seg_start;
+    sv.seg_adapter = seg_adapter;
+    sv.seg_rank = seg_rank;
+    sv.seg_scale = seg_scale;
+    sv.token_index = token_index;
+    sv.n_seg_dev = nullptr;
+    sv.n_seg = n_seg;
+  }
+  if (!decode_supported(n_tokens, lora_on ? n_seg : 0, pool->d_out, pool->max_rank))
+    return MLORA_ERR_SHAPE;
+  return run_linear(x, W_fp8, pool, sv, n_tokens, lora_on, y, (char*)workspace, stream, w_scale);
 }
 
 int mlora_build_segments(const int32_t* token_adapter, const float* adapter_scale, int n_tokens,

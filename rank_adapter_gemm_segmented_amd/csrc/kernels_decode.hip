@@ -59,7 +59,31 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <int TT>
+// Eight FP8 e4m3 codes (OCP E4M3: bias 7, subnormals m/8 * 2^-6) -> eight
+// bf16 values, exact: every e4m3 value has at most 4 significant bits and an
+// exponent inside bf16's range. gfx950's scaled conversion turns two codes
+// into two bf16 per instruction (scale 1; checked against the E4M3
+// definition on all 256 codes).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, HI));
+}
+__device__ __forceinline__ u32x4_t e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  u32x4_t r;
+  r.x = e4m3x2_to_bf16x2<false>(lo);
+  r.y = e4m3x2_to_bf16x2<true>(lo);
+  r.z = e4m3x2_to_bf16x2<false>(hi);
+  r.w = e4m3x2_to_bf16x2<true>(hi);
+  return r;
+}
+
+// W8: W holds FP8 e4m3 codes (one byte per element, a float32 scale per row
+// applied by k_finish). A lane's 16-byte load then covers 16 columns, which
+// serve two consecutive k-steps: lane group g = l / 16 of the step pair
+// (2q, 2q + 1) starting at column C takes columns C + 16 g .. + 7 in step 2q
+// and C + 16 g + 8 .. + 15 in step 2q + 1, and reads x at the same columns.
+template <int TT, bool W8>
 __global__ __launch_bounds__(kDecThreads) void k_stream_bf16(DecodeArgs a) {
   constexpr int NTB = TT / 16;
   constexpr int XP = kDecXPitch;
@@ -142,18 +166,31 @@ __global__ __launch_bounds__(kDecThreads) void k_stream_bf16(DecodeArgs a) {
   // loaded value.
   const int rb = wave & 3, kh = wave >> 2;
   const int nrow = tile * kDecRows + rb * 16 + l16;
-  const int half_steps = (nks + 1) / 2;
+  // (FP8: the first half ends on an even step, so no step pair straddles the halves)
+  const int half_steps = W8 ? (((nks + 1) / 2 + 1) & ~1) : (nks + 1) / 2;
   const int ks_begin = kh ? half_steps : 0;
   const int ks_end = kh ? nks : half_steps;
   const uint16_t* wrow = W + (long long)min(nrow, d_out - 1) * d_in + k0;
+  const uint8_t* wrow8 = (const uint8_t*)a.W + (long long)min(nrow, d_out - 1) * d_in + k0;
   u32x4_t wr[kDecWSteps];
   auto load_w = [&](int s) {
     // steps of the other k-half read the pool's zero block (address select)
-    const int k = (ks_begin + s) * 32 + kq;
-    wr[s] = ld_nt16(ks_begin + s < ks_end ? wrow + min(k, kc - 8) : (const uint16_t*)a.pv.zeros + kq);
+    if constexpr (W8) {   // slot s holds step pair (2s, 2s + 1)
+      const int k = (ks_begin + 2 * s) * 32 + 2 * kq;
+      wr[s] = ld_nt16(ks_begin + 2 * s < ks_end ? (const void*)(wrow8 + min(k, kc - 16))
+                                                : (const void*)((const uint16_t*)a.pv.zeros + kq));
+    } else {
+      const int k = (ks_begin + s) * 32 + kq;
+      wr[s] = ld_nt16(ks_begin + s < ks_end ? wrow + min(k, kc - 8) : (const uint16_t*)a.pv.zeros + kq);
+    }
   };
+  // FP8: the 16 steps are 8 loads; half of them are requested ahead of the
+  // x barrier, as for the bf16 weight (8 ahead: 16.7 us LoRA-on, 4: 16.2 us,
+  // 2: 16.5 us on the decode batch)
+  constexpr int kWLoads = W8 ? kDecWSteps / 2 : kDecWSteps;
+  constexpr int kWPre = W8 ? kWLoads / 2 : kDecWPre;
 #pragma unroll
-  for (int s = 0; s < kDecWPre; ++s) load_w(s);
+  for (int s = 0; s < kWPre; ++s) load_w(s);
   // nothing below is hoisted between these loads (it would wait for the
   // metadata before the last of them are issued)
   __builtin_amdgcn_sched_barrier(0);
@@ -221,14 +258,28 @@ __global__ __launch_bounds__(kDecThreads) void k_stream_bf16(DecodeArgs a) {
   for (int tb = 0; tb < NTB; ++tb) acc[tb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < kDecWSteps; ++s) {
-    if (s + kDecWPre < kDecWSteps) load_w(s + kDecWPre);
+    if constexpr (W8) {
+      if ((s & 1) == 0 && s / 2 + kWPre < kWLoads) load_w(s / 2 + kWPre);
+    } else {
+      if (s + kDecWPre < kDecWSteps) load_w(s + kDecWPre);
+    }
     // x columns past ks_end (past the chunk) are zero in LDS; k-steps past
     // the LDS chunk are clamped onto such columns
-    const int ks = min(ks_begin + s, kDecMaxKc / 32 - 1);
+    int xc;
+    u32x4_t wop;
+    if constexpr (W8) {
+      const int kp = min(ks_begin + (s & ~1), kDecMaxKc / 32 - 2);   // the step pair's first step
+      xc = kp * 32 + 2 * kq + 8 * (s & 1);
+      const u32x4_t raw = wr[s / 2];
+      wop = (s & 1) ? e4m3x8_to_bf16x8(raw.z, raw.w) : e4m3x8_to_bf16x8(raw.x, raw.y);
+    } else {
+      xc = min(ks_begin + s, kDecMaxKc / 32 - 1) * 32 + kq;
+      wop = wr[s];
+    }
 #pragma unroll
     for (int tb = 0; tb < NTB; ++tb) {
-      const u32x4_t xo = *(const u32x4_t*)&sm.xs[(tb * 16 + l16) * XP + ks * 32 + kq];
-      acc[tb] = mfma16d(wr[s], xo, acc[tb]);
+      const u32x4_t xo = *(const u32x4_t*)&sm.xs[(tb * 16 + l16) * XP + xc];
+      acc[tb] = mfma16d(wop, xo, acc[tb]);
     }
     __builtin_amdgcn_sched_barrier(0);   // keep each step's load next to its MFMAs
   }
@@ -317,7 +368,7 @@ __global__ __launch_bounds__(kDecThreads) void k_stream_bf16(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 constexpr int kFinUnroll = 8;
 
-template <int TT>
+template <int TT, bool W8>
 __global__ __launch_bounds__(256) void k_finish_bf16(DecodeArgs a) {
   constexpr int NTB = TT / 16;
   constexpr int kPre = 2;                // B column groups of 8 prefetched (ranks <= 16)
@@ -342,6 +393,12 @@ __global__ __launch_bounds__(256) void k_finish_bf16(DecodeArgs a) {
   f32x4_t p[kFinUnroll];
 #pragma unroll
   for (int u = 0; u < kFinUnroll; ++u) p[u] = *(const f32x4_t*)(pbase + min(u, a.n_chunks - 1) * cstride);
+  // FP8 weight: the row scales of the lane's 4 rows
+  float wsc[4] = {1.f, 1.f, 1.f, 1.f};
+  if constexpr (W8) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) wsc[v] = a.w_scale[min(n + v, d_out - 1)];
+  }
 
   // v of the 16 tokens: sum of the stream kernel's slices [c][w]. A 16-byte
   // quad of one token is element e; G groups of threads each sum every G-th
@@ -405,6 +462,11 @@ __global__ __launch_bounds__(256) void k_finish_bf16(DecodeArgs a) {
         acc[2] += p[u][2];
         acc[3] += p[u][3];
       }
+  }
+
+  if constexpr (W8) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) acc[v] *= wsc[v];
   }
 
   if (lora) {
@@ -516,16 +578,17 @@ void decode_plan(int d_in, int d_out, int* n_tiles, int* kc, int* n_chunks) {
   *n_chunks = (d_in + k - 1) / k;
 }
 
-template <int TT>
+template <int TT, bool W8>
 static void launch_decode_tt(const DecodeArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_stream_bf16<TT>, dim3(a.n_tiles * a.n_chunks), dim3(kDecThreads), 0, st, a);
-  hipLaunchKernelGGL(k_finish_bf16<TT>, dim3(a.n_tiles * (TT / 16)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((k_stream_bf16<TT, W8>), dim3(a.n_tiles * a.n_chunks), dim3(kDecThreads), 0, st, a);
+  hipLaunchKernelGGL((k_finish_bf16<TT, W8>), dim3(a.n_tiles * (TT / 16)), dim3(256), 0, st, a);
 }
 
 void launch_decode_bf16(const DecodeArgs& a, hipStream_t st) {
-  if (a.T <= 16) launch_decode_tt<16>(a, st);
-  else if (a.T <= 32) launch_decode_tt<32>(a, st);
-  else launch_decode_tt<64>(a, st);
+  const bool w8 = a.w_scale != nullptr;
+  if (a.T <= 16) w8 ? launch_decode_tt<16, true>(a, st) : launch_decode_tt<16, false>(a, st);
+  else if (a.T <= 32) w8 ? launch_decode_tt<32, true>(a, st) : launch_decode_tt<32, false>(a, st);
+  else w8 ? launch_decode_tt<64, true>(a, st) : launch_decode_tt<64, false>(a, st);
 }
 
 }  // namespace mlora

@@ -49,6 +49,7 @@ struct DecodeArgs {
   int kc;          // d_in chunk width (multiple of 64)
   int n_chunks;    // ceil(d_in / kc)
   int unit_rows;   // rank rows per shrink unit (4, 8 or 16)
+  const float* w_scale;   // FP8 weight: float32 scale per W row (W holds e4m3 codes); null: bf16 W
 };
 
 // Merge of one adapter into a base weight: W_out = W_in + scale * B A.
