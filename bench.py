@@ -67,6 +67,8 @@ def parse():
     ap.add_argument("--proj", default="q", help="prefill projection (also the merge shape)")
     ap.add_argument("--rank", type=int, default=64, help="adapter rank of the merge workload")
     ap.add_argument("--rotate-gib", type=float, default=1.0)
+    ap.add_argument("--graph", action="store_true",
+                    help="time the K calls as HIP-graph replays (eager times are reported too)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time (wall x threads) of the oracle baseline")
@@ -127,6 +129,47 @@ def ingest_counters(workload: str, kernels, fetch_csv: str, write_csv: str) -> d
         json.dump(allt, fh, indent=1, sort_keys=True)
         fh.write("\n")
     return out
+
+
+def graph_timed(step, n_sets: int, steps: int, warmup: int) -> float:
+    """ms per step over exactly `steps` calls replayed from HIP graphs: one
+    graph holds n_sets consecutive calls (one per buffer set), a second one
+    the remainder. Launch costs on the host drop out; the GPU runs the
+    kernels back to back. Warm-up calls run eagerly first (and on the
+    capture's side stream, as capture wants)."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(max(warmup, 1)):
+            step(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    full, tail = steps // n_sets, steps % n_sets
+    g_full, g_tail = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    if full:
+        with torch.cuda.graph(g_full):
+            for i in range(n_sets):
+                step(i)
+    if tail:
+        with torch.cuda.graph(g_tail):
+            for i in range(tail):
+                step(i)
+    if full:
+        g_full.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(full):
+        g_full.replay()
+    if tail:
+        g_tail.replay()
+    e1.record(stream)
+    e1.synchronize()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
 
 
 def counted_traffic(workload: str):
@@ -553,9 +596,19 @@ def bench_fp8w(args):
         torch.cuda.synchronize()
         print(f"[bench] calibration copy of {n} bytes done", file=sys.stderr, flush=True)
         return
-    ms_on = timed(1, args.steps, args.warmup)
-    ms_off = timed(0, args.steps, args.warmup)
-    print(f"[bench] decode_fp8w: lora_on {ms_on * 1e3:.2f} us/step, lora_off {ms_off * 1e3:.2f} us/step, "
+    ms_on_eager = timed(1, args.steps, args.warmup)
+    ms_off_eager = timed(0, args.steps, args.warmup)
+    ms_on, ms_off = ms_on_eager, ms_off_eager
+    if args.graph:
+        def gstep(lora_on):
+            def f(i):
+                W8, sc, pool, y, ws = sets[i % n_sets]
+                ml.linear_fp8w(x0, W8, sc, pool, *meta, lora_on=lora_on, out=y, workspace=ws)
+            return f
+        ms_on = graph_timed(gstep(1), n_sets, args.steps, args.warmup)
+        ms_off = graph_timed(gstep(0), n_sets, args.steps, args.warmup)
+    print(f"[bench] decode_fp8w: lora_on {ms_on * 1e3:.2f} us/step, lora_off {ms_off * 1e3:.2f} us/step "
+          f"({'graph replay' if args.graph else 'eager'}; eager {ms_on_eager * 1e3:.2f} / {ms_off_eager * 1e3:.2f}), "
           f"{n_sets} buffer sets", file=sys.stderr, flush=True)
     gbs_on = bytes_on / (ms_on * 1e-3) / 1e9
     out = {
@@ -569,6 +622,8 @@ def bench_fp8w(args):
                    "unique_bytes_lora_on": bytes_on, "unique_bytes_lora_off": bytes_off},
         "lora_off": {"ms_per_step": round(ms_off, 6), "gbs": round(bytes_off / (ms_off * 1e-3) / 1e9, 1)},
         "lora_on_overhead": round(ms_on / ms_off - 1.0, 4),
+        "timing": "K calls replayed from HIP graphs" if args.graph else "K eager calls",
+        "eager": {"ms_per_step_lora_on": round(ms_on_eager, 6), "ms_per_step_lora_off": round(ms_off_eager, 6)},
         "roofline": {"bound": "hbm", "achieved": round(gbs_on, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs_on / HBM_PEAK_GBS, 4), "traffic": counted_traffic("decode_fp8w"),
                      "algorithmic_bytes": bytes_on, "us_per_call": round(ms_on * 1e3, 3),
@@ -685,9 +740,14 @@ def main():
         print(f"[bench] calibration copy of {n} bytes done", file=sys.stderr, flush=True)
         return
 
-    ms_on = timed(1, args.steps, args.warmup)
-    ms_off = timed(0, args.steps, args.warmup)
-    print(f"[bench] {case.name}: lora_on {ms_on * 1e3:.2f} us/step, lora_off {ms_off * 1e3:.2f} us/step, "
+    ms_on_eager = timed(1, args.steps, args.warmup)
+    ms_off_eager = timed(0, args.steps, args.warmup)
+    ms_on, ms_off = ms_on_eager, ms_off_eager
+    if args.graph:
+        ms_on = graph_timed(lambda i: step(i, 1), n_sets, args.steps, args.warmup)
+        ms_off = graph_timed(lambda i: step(i, 0), n_sets, args.steps, args.warmup)
+    print(f"[bench] {case.name}: lora_on {ms_on * 1e3:.2f} us/step, lora_off {ms_off * 1e3:.2f} us/step "
+          f"({'graph replay' if args.graph else 'eager'}; eager {ms_on_eager * 1e3:.2f} / {ms_off_eager * 1e3:.2f}), "
           f"{n_sets} buffer sets of {set_bytes / 2**20:.1f} MiB", file=sys.stderr, flush=True)
 
     gbs_on = bytes_on / (ms_on * 1e-3) / 1e9
@@ -755,6 +815,9 @@ def main():
                      "pct_hbm_roofline": round(100 * gbs_off / HBM_PEAK_GBS, 2)},
         "lora_on_overhead": round(ms_on / ms_off - 1.0, 4),
         "byte_floor_ratio": round(bytes_on / bytes_off, 4),
+        "timing": ("K calls replayed from HIP graphs (one graph per pass over the buffer sets)"
+                   if args.graph else "K eager calls through the Python binding"),
+        "eager": {"ms_per_step_lora_on": round(ms_on_eager, 6), "ms_per_step_lora_off": round(ms_off_eager, 6)},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
