@@ -79,11 +79,17 @@ def _check(code: int, what: str):
 
 
 def _ptr(t: Optional[torch.Tensor]):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    # plain ints (ctypes passes them as void*): no wrapper object per argument
+    return None if t is None else t.data_ptr()
+
+
+_raw_stream = torch._C._cuda_getCurrentRawStream
 
 
 def _stream():
-    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    """The current torch stream of the current device as a raw HIP stream
+    handle (also the capture stream inside torch.cuda.graph)."""
+    return _raw_stream(torch.cuda.current_device())
 
 
 def _dtype_code(dt: torch.dtype) -> int:
