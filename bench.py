@@ -794,11 +794,27 @@ def main():
             if reps >= 50:
                 break
         t_batch = t_total / reps * (T / n_rows)
+        # the same sample on one thread, once (outputs are bitwise the same at any thread count)
+        rows1 = rows if rows is not None else np.arange(min(T, max(1, n_rows // 4)), dtype=np.int32)
+        t0 = time.perf_counter()
+        oracle.case_linear(case, 1, rows=rows1, threads=1, pool=pool_o)
+        t_1 = (time.perf_counter() - t0) * (T / len(rows1))
+        cpu_model = ""
+        try:
+            with open("/proc/cpuinfo") as fh:
+                cpu_model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "")
+        except OSError:
+            pass
         cpu = {"value": round(bytes_on / t_batch / 1e9, 4), "unit": "GB/s", "cores": threads,
                "kind": "oracle",
                "sample": f"{n_rows} of {T} rows of the {case.name} batch, lora_on=1, fp64, "
                          f"{reps} repetitions, {t_total:.1f} s wall; value scaled to the whole batch",
-               "seconds_per_batch": round(t_batch, 4)}
+               "seconds_per_batch": round(t_batch, 4),
+               "single_thread": {"seconds_per_batch": round(t_1, 4),
+                                 "value": round(bytes_on / t_1 / 1e9, 4),
+                                 "sample": f"{len(rows1)} rows, once, scaled to the whole batch"},
+               "gflops_fp64": round(flops_on / t_batch / 1e9, 2),
+               "cpu_model": cpu_model}
 
     cfg = {"workload": case.name, "tokens": T, "d_in": d_in, "d_out": d_out,
            "adapters_touched": len(touched), "segments": case.n_seg if case.sorted_input else None,
