@@ -104,7 +104,8 @@ int mlora_pool_destroy(mlora_pool_t pool);
  * hipMemcpyKind "default"). The copy is stream-ordered: a later mlora_linear on
  * the same stream sees the adapter, and A and B may be reused once the stream
  * has passed this call. Errors: MLORA_ERR_ADAPTER (id out of range),
- * MLORA_ERR_EXISTS (slot occupied), MLORA_ERR_RANK (rank < 1 or > max_rank). */
+ * MLORA_ERR_EXISTS (slot occupied), MLORA_ERR_RANK (rank < 1 or > max_rank),
+ * MLORA_ERR_SHAPE (the pool holds fused adapters: see below). */
 int mlora_register_adapter(mlora_pool_t pool, int adapter_id, int rank, const void* A,
                            const void* B, hipStream_t stream);
 
@@ -121,12 +122,17 @@ int mlora_register_adapter(mlora_pool_t pool, int adapter_id, int rank, const vo
  * part of v. mlora_linear then computes, for every slice at once,
  *     y[:, slice m] = W_m x + scale_s * B_m (A_m x)
  * with one scale per segment shared by the slices. Segments name the
- * adapter with seg_rank = R. The zero blocks of B are read by the expand
- * (R / slice rank times the B bytes of separate calls). n_slices in
+ * adapter with seg_rank = R. A pool holds either plain adapters or fused
+ * ones over one stacking of W: its first fused registration fixes the slice
+ * rows, and later ones must repeat them. When every fused adapter of the
+ * pool has equal slice ranks (one rank per adapter config), the expand of a
+ * row tile inside one slice reads only that slice's rank columns; otherwise
+ * it reads all R columns, zero blocks included. n_slices in
  * 1 .. MLORA_MAX_SLICES; slice_rows, slice_ranks, A and B are host arrays
  * (A[m], B[m] host or device pointers, copied as in mlora_register_adapter).
  * Errors as mlora_register_adapter, plus MLORA_ERR_SHAPE (slice rows do not
- * add up to d_out) and MLORA_ERR_RANK (R > max_rank). */
+ * add up to d_out, the pool holds plain adapters, or its fused adapters
+ * stack W differently) and MLORA_ERR_RANK (R > max_rank). */
 #define MLORA_MAX_SLICES 8
 int mlora_register_adapter_fused(mlora_pool_t pool, int adapter_id, int n_slices,
                                  const int* slice_rows, const int* slice_ranks,

@@ -22,6 +22,12 @@ struct mlora_pool_s {
   int32_t* dev_rank = nullptr;
   void* zeros = nullptr;     // kZeroBytes of zeros, never written after creation
   std::vector<int> host_rank;
+  // 0: no adapter registered yet; 1: plain adapters; 2: fused adapters over
+  // stacked projections (the pool keeps the row slicing of its first one)
+  int kind = 0;
+  int n_slices = 0;          // row slicing of a fused pool (0: none)
+  int slice_end[MLORA_MAX_SLICES] = {};
+  bool slice_uniform = true; // every fused adapter so far has equal slice ranks
 };
 
 namespace {
@@ -96,6 +102,8 @@ PoolView view_of(const mlora_pool_s* p) {
   v.b_offset = p->b_offset;
   v.capacity = p->capacity;
   v.max_rank = p->max_rank;
+  v.n_slices = (p->kind == 2 && p->slice_uniform) ? p->n_slices : 0;
+  for (int m = 0; m < 8; ++m) v.slice_end[m] = m < p->n_slices ? p->slice_end[m] : 0;
   return v;
 }
 
@@ -251,6 +259,7 @@ int mlora_register_adapter(mlora_pool_t p, int adapter_id, int rank, const void*
   if (adapter_id < 0 || adapter_id >= p->capacity) return MLORA_ERR_ADAPTER;
   if (rank < 1 || rank > p->max_rank) return MLORA_ERR_RANK;
   if (p->host_rank[adapter_id] != 0) return MLORA_ERR_EXISTS;
+  if (p->kind == 2) return MLORA_ERR_SHAPE;   // a pool of fused adapters takes fused ones only
   char* slot = (char*)p->base + (size_t)adapter_id * (size_t)p->slot_elems * p->elem;
   // A: [rank, d_in] contiguous
   hipError_t e = hipMemcpyAsync(slot, A, (size_t)rank * p->d_in * p->elem, hipMemcpyDefault, stream);
@@ -269,6 +278,7 @@ int mlora_register_adapter(mlora_pool_t p, int adapter_id, int rank, const void*
   launch_set_slot_rank(p->dev_rank, adapter_id, rank, stream);
   if (check_launch() != MLORA_OK) return MLORA_ERR_HIP;
   p->host_rank[adapter_id] = rank;
+  p->kind = 1;
   return MLORA_OK;
 }
 
@@ -290,6 +300,14 @@ int mlora_register_adapter_fused(mlora_pool_t p, int adapter_id, int n_slices, c
     if (rank > p->max_rank) return MLORA_ERR_RANK;
   }
   if (rows != p->d_out) return MLORA_ERR_SHAPE;
+  if (p->kind == 1) return MLORA_ERR_SHAPE;   // a pool of plain adapters takes plain ones only
+  if (p->kind == 2) {                          // the pool's W stacks the same projections
+    if (n_slices != p->n_slices) return MLORA_ERR_SHAPE;
+    for (int m = 0, end = 0; m < n_slices; ++m) {
+      end += slice_rows[m];
+      if (end != p->slice_end[m]) return MLORA_ERR_SHAPE;
+    }
+  }
   char* slot = (char*)p->base + (size_t)adapter_id * (size_t)p->slot_elems * p->elem;
   char* bdst = slot + (size_t)p->b_offset * p->elem;
   const int bld = (rank + 7) & ~7;
@@ -312,6 +330,13 @@ int mlora_register_adapter_fused(mlora_pool_t p, int adapter_id, int n_slices, c
   launch_set_slot_rank(p->dev_rank, adapter_id, rank, stream);
   if (check_launch() != MLORA_OK) return MLORA_ERR_HIP;
   p->host_rank[adapter_id] = rank;
+  if (p->kind != 2) {
+    p->kind = 2;
+    p->n_slices = n_slices;
+    for (int m = 0, end = 0; m < n_slices; ++m) p->slice_end[m] = (end += slice_rows[m]);
+  }
+  for (int m = 1; m < n_slices; ++m)
+    if (slice_ranks[m] != slice_ranks[0]) p->slice_uniform = false;
   return MLORA_OK;
 }
 

@@ -71,7 +71,33 @@ struct PoolView {
   long long b_offset;      // element offset of B inside a slot (= max_rank * d_in)
   int capacity;
   int max_rank;
+  // Stacked projections (a pool of fused adapters): W's rows fall into
+  // n_slices slices ending at slice_end[m]; an adapter of rank R holds slice
+  // m's rank columns [m R / n_slices, (m + 1) R / n_slices) and zeros
+  // elsewhere in those rows. n_slices = 0: no slicing (or slices of unequal
+  // rank), every rank column may be nonzero.
+  int n_slices;
+  int slice_end[8];
 };
+
+// Rank columns [*w0, *w1) that can be nonzero in rows [r0, r1) for an
+// adapter of rank R: one slice's window when the rows lie inside one slice,
+// else all of [0, R).
+__device__ __forceinline__ void slice_window(const PoolView& pv, int r0, int r1, int R, int* w0, int* w1) {
+  *w0 = 0;
+  *w1 = R;
+  int start = 0;
+  for (int m = 0; m < pv.n_slices && m < 8; ++m) {
+    const int end = pv.slice_end[m];
+    if (r0 >= start && r1 <= end) {
+      const int rs = R / pv.n_slices;
+      *w0 = m * rs;
+      *w1 = (m + 1) * rs;
+      return;
+    }
+    start = end;
+  }
+}
 
 // Metadata of one call over sorted positions.
 struct SegView {

@@ -368,7 +368,10 @@ __global__ __launch_bounds__(kDecThreads) void k_stream_bf16(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 constexpr int kFinUnroll = 8;
 
-template <int TT, bool W8>
+// SL: the pool holds fused adapters over stacked projections (expand only
+// the tile's slice window; a template flag, so plain pools keep a loop that
+// starts at column 0: a run-time start measured 1 us slower)
+template <int TT, bool W8, bool SL>
 __global__ __launch_bounds__(256) void k_finish_bf16(DecodeArgs a) {
   constexpr int NTB = TT / 16;
   constexpr int kPre = 2;                // B column groups of 8 prefetched (ranks <= 16)
@@ -434,12 +437,21 @@ __global__ __launch_bounds__(256) void k_finish_bf16(DecodeArgs a) {
   const uint16_t* Bb = (const uint16_t*)(live ? a.pv.base : a.pv.zeros) +
                        (live ? (long long)ad * a.pv.slot_elems + a.pv.b_offset : 0);
   const int bld = live ? round_up8(r) : 0;
+  // a fused adapter over stacked projections: only the tile's slice window
+  // of rank columns can be nonzero in its rows (from column jb, a multiple of 8)
+  int jb = 0, je = r;
+  if constexpr (SL) {
+    int w0 = 0, w1 = r;
+    if (live) slice_window(a.pv, tile * kDecRows, min(tile * kDecRows + kDecRows, d_out), r, &w0, &w1);
+    jb = w0 & ~7;
+    je = min(w1, r);
+  }
   u32x4_t b8[kPre][4];
 #pragma unroll
   for (int g = 0; g < kPre; ++g)
 #pragma unroll
     for (int v = 0; v < 4; ++v)
-      b8[g][v] = ld16(Bb + (live ? (long long)min(n + v, d_out - 1) * bld + min(8 * g, bld - 8) : 0));
+      b8[g][v] = ld16(Bb + (live ? (long long)min(n + v, d_out - 1) * bld + min(jb + 8 * g, bld - 8) : 0));
 
   // chunk partials summed in chunk order
   f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -506,11 +518,11 @@ __global__ __launch_bounds__(256) void k_finish_bf16(DecodeArgs a) {
     if (live) {
       const float* vv = vs[lane % 16];
       float lsum[4] = {0.f, 0.f, 0.f, 0.f};
-      for (int j0 = 0; j0 < r; j0 += 8) {
+      for (int j0 = jb; j0 < je; j0 += 8) {
         u32x4_t bq[4];
-        if (j0 < 8 * kPre) {
+        if (j0 - jb < 8 * kPre) {
 #pragma unroll
-          for (int v = 0; v < 4; ++v) bq[v] = b8[j0 / 8 == 0 ? 0 : kPre - 1][v];
+          for (int v = 0; v < 4; ++v) bq[v] = b8[j0 - jb < 8 ? 0 : kPre - 1][v];
         } else {
 #pragma unroll
           for (int v = 0; v < 4; ++v) bq[v] = ld16(Bb + (long long)min(n + v, d_out - 1) * bld + j0);
@@ -581,7 +593,10 @@ void decode_plan(int d_in, int d_out, int* n_tiles, int* kc, int* n_chunks) {
 template <int TT, bool W8>
 static void launch_decode_tt(const DecodeArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((k_stream_bf16<TT, W8>), dim3(a.n_tiles * a.n_chunks), dim3(kDecThreads), 0, st, a);
-  hipLaunchKernelGGL((k_finish_bf16<TT, W8>), dim3(a.n_tiles * (TT / 16)), dim3(256), 0, st, a);
+  if (a.lora_on && a.pv.n_slices > 0)
+    hipLaunchKernelGGL((k_finish_bf16<TT, W8, true>), dim3(a.n_tiles * (TT / 16)), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_finish_bf16<TT, W8, false>), dim3(a.n_tiles * (TT / 16)), dim3(256), 0, st, a);
 }
 
 void launch_decode_bf16(const DecodeArgs& a, hipStream_t st) {

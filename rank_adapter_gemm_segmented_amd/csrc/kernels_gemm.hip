@@ -617,17 +617,24 @@ void k_gemm2(LinearArgs a) {
       // takes run k0 + l and writes one descriptor per 16 rank columns it has
       // in this chunk: {rs | re << 16, jc, adapter, B row pitch}. A pass
       // lists at most kEpiMaxUnits units; longer lists take further passes.
+      // A fused adapter over stacked projections is nonzero in this wave's
+      // rows only in its slice's window of rank columns; units cover that
+      // window (rounded out to 16 columns, whose extra columns are zero).
+      const int wr0 = r0 + wr * WR, wr1 = min(wr0 + WR, d_out);
       for (int pb = 0;; pb += kEpiMaxUnits) {
       int nu_tot = 0;                                // units of the chunk (uniform)
       for (int k0 = 0; k0 < nrw; k0 += kWave) {
         const int k = k0 + lane;
-        int rs = 0, re = 0, ad = -1, pitch = 0, cnt = 0;
+        int rs = 0, re = 0, ad = -1, pitch = 0, cnt = 0, lo = 0;
         if (k < nrw) {
           rs = wstart[wave][k];
           re = wstart[wave][k + 1];
           const int4 pi = pinfo[rs];
-          const int rk = pi.y >= 0 ? min(pi.z - jc0, rc) : 0;
-          cnt = rk > 0 ? (rk + 15) / 16 : 0;
+          int w0 = 0, w1 = pi.z;
+          if (pi.y >= 0) slice_window(a.pv, wr0, wr1, pi.z, &w0, &w1);
+          lo = max(w0 - jc0, 0) & ~15;
+          const int hi = pi.y >= 0 ? min(min(w1, pi.z) - jc0, rc) : 0;
+          cnt = hi > lo ? (hi - lo + 15) / 16 : 0;
           ad = pi.y;
           pitch = round_up8(pi.z);
         }
@@ -640,7 +647,7 @@ void k_gemm2(LinearArgs a) {
         const int base = nu_tot + inc - cnt;
         for (int i = 0; i < cnt; ++i) {
           const int g = base + i - pb;
-          if (g >= 0 && g < kEpiMaxUnits) udesc[wave][g] = make_int4(rs | (re << 16), 16 * i, ad, pitch);
+          if (g >= 0 && g < kEpiMaxUnits) udesc[wave][g] = make_int4(rs | (re << 16), lo + 16 * i, ad, pitch);
         }
         nu_tot += __builtin_amdgcn_readfirstlane(__shfl(inc, kWave - 1, kWave));
       }

@@ -42,7 +42,8 @@ class FusedDeviceCase:
         self.ws = self.pool.workspace(c0.n_tokens)
         self.seg_start = i32(c0.seg_start)
         self.seg_adapter = i32(c0.seg_adapter)
-        self.seg_rank = i32(np.where(c0.seg_adapter >= 0, c0.seg_rank * n, 0))
+        # a segment's rank is its adapter's stacked rank (the slices' ranks added)
+        self.seg_rank = i32(np.where(c0.seg_adapter >= 0, sum(c.seg_rank for c in slices), 0))
         self.seg_scale = f32(c0.seg_scale)
 
     def run(self, lora_on):
@@ -114,6 +115,45 @@ def test_fused_registration_errors():
     with pytest.raises(ml.MloraError) as e:
         pool.register_fused(1, [(A, B), (A, B)])
     assert e.value.code == E["MLORA_ERR_EXISTS"]
+    # the pool's W stacks 24 + 24 rows now: other slicings and plain adapters are refused
+    with pytest.raises(ml.MloraError) as e:
+        pool.register_fused(0, [(A, B[:16]), (A, torch.zeros(32, 8, dtype=torch.bfloat16, device="cuda"))])
+    assert e.value.code == E["MLORA_ERR_SHAPE"]
+    with pytest.raises(ml.MloraError) as e:
+        pool.register(0, A, torch.zeros(48, 8, dtype=torch.bfloat16, device="cuda"))
+    assert e.value.code == E["MLORA_ERR_SHAPE"]
+    plain = ml.Pool(64, 48, torch.bfloat16, 16, 2)
+    plain.register(0, A, torch.zeros(48, 8, dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(ml.MloraError) as e:          # and a pool of plain adapters takes no fused one
+        plain.register_fused(1, [(A, B), (A, B)])
+    assert e.value.code == E["MLORA_ERR_SHAPE"]
+
+
+def _custom_slices(seed, d_in, rows, ranks_per_slice, ids, n_ad):
+    from mlora_inputs import make_custom_case
+    import dataclasses
+    cs = [make_custom_case(seed + m, "bf16", d_in, rows[m], ids, {a: ranks_per_slice[m] for a in range(n_ad)})
+          for m in range(len(rows))]
+    return [cs[0]] + [dataclasses.replace(c, x=cs[0].x) for c in cs[1:]]
+
+
+@pytest.mark.parametrize("T", [40, 200])
+@pytest.mark.parametrize("layout", ["unequal_ranks", "straddling_tiles"])
+def test_fused_slicing_cases(T, layout):
+    # unequal slice ranks turn the window off for the pool; slice boundaries
+    # inside a row tile keep that tile's full rank range; both stay exact
+    ids = sorted(np.random.default_rng(T).integers(-1, 6, size=T).tolist())
+    if layout == "unequal_ranks":
+        slices = _custom_slices(700, 512, [256, 64, 64], [16, 8, 8], ids, 6)
+    else:
+        slices = _custom_slices(710, 512, [200, 72, 136], [16, 16, 16], ids, 6)
+    log(f"[fused] {layout}, T={T}, rows {[c.d_out for c in slices]}")
+    dc = FusedDeviceCase(slices)
+    for lora_on in (1, 0):
+        y = y_host(dc.run(lora_on))
+        y_ref = oracle.fused_case_linear(slices, lora_on, threads=oracle_threads())
+        worst = compare(y, y_ref, BF16_TOL, f"{layout} T={T} lora_on={lora_on}")
+        log(f"  lora_on={lora_on}: max err/bound {worst:.3f}")
 
 
 def test_fused_unsorted_batch():
