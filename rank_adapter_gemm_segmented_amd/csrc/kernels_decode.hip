@@ -407,14 +407,33 @@ __global__ __launch_bounds__(256) void k_finish_bf16(DecodeArgs a) {
   // quad of one token is element e; G groups of threads each sum every G-th
   // slice of an element, then the groups are added in group order. The first
   // batch of slice loads is issued here, with the partials still in flight.
-  const int nq = a.r_ws / 4;
-  const int E = 16 * nq;
+  // Rank quads summed and staged: all of them; for a fused pool only quads
+  // [q0, q0 + nqv), the union over the block's 16 tokens of their windows in
+  // this tile's slice, widened to multiples of 8 columns (the expand reads
+  // v in groups of 8 from the window start rounded down to 8). Every wave
+  // holds the same 16 tokens, so the union is the same in every wave.
+  int q0 = 0, nqv = a.r_ws / 4;
+  if constexpr (SL) {
+    const int ad_ = pe.x, r_ = min(pe.y, a.pv.max_rank);
+    const bool live_ = lora && ad_ >= 0 && ad_ < a.pv.capacity && r_ > 0 && t < T;
+    int w0 = 0, w1 = r_;
+    if (live_) slice_window(a.pv, tile * kDecRows, min(tile * kDecRows + kDecRows, d_out), r_, &w0, &w1);
+    int lo = live_ ? (w0 & ~7) : 0x7fffffff, hi = live_ ? min(w1, r_) : 0;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      lo = min(lo, __shfl_xor(lo, off, kWave));
+      hi = max(hi, __shfl_xor(hi, off, kWave));
+    }
+    q0 = hi > lo ? lo / 4 : 0;
+    nqv = hi > lo ? round_up8(hi) / 4 - q0 : 1;
+  }
+  const int E = 16 * nqv;
   const int G = E >= 256 ? 1 : E >= 128 ? 2 : 4;
   const int nsl = a.n_chunks * kDecWaves;
   const long long vstride = (long long)T * a.r_ws;
   auto vptr = [&](int e0) {
     const int e = min(e0 + tid / G, E - 1);
-    return a.v_part + (long long)min(tb * 16 + e / nq, T - 1) * a.r_ws + 4 * (e % nq);
+    return a.v_part + (long long)min(tb * 16 + e / nqv, T - 1) * a.r_ws + 4 * (q0 + e % nqv);
   };
   f32x4_t vq[kFinUnroll];
   {
@@ -511,7 +530,7 @@ __global__ __launch_bounds__(256) void k_finish_bf16(DecodeArgs a) {
           tot[3] += vgrp[gg][tid][3];
         }
         const int ee = e0 + tid;
-        *(f32x4_t*)&vs[ee / nq][4 * (ee % nq)] = tot;
+        *(f32x4_t*)&vs[ee / nqv][4 * (q0 + ee % nqv)] = tot;
       }
       lds_barrier();
     }
