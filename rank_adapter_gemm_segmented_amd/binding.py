@@ -143,7 +143,9 @@ class Pool:
     def register_fused(self, adapter_id: int, slices):
         """``mlora_register_adapter_fused``: one adapter over stacked projections.
         ``slices`` is a list of (A_m [r_m, d_in], B_m [rows_m, r_m]) in the
-        order the projections are stacked in W."""
+        order the projections are stacked in W. A pool holds either plain or
+        fused adapters, and all fused ones stack W the same way; segments
+        name the adapter with the stacked rank sum(r_m)."""
         n = len(slices)
         rows = (ctypes.c_int * n)(*[int(B.shape[0]) for _, B in slices])
         ranks = (ctypes.c_int * n)(*[int(A.shape[0]) for A, _ in slices])
