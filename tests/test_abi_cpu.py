@@ -87,3 +87,14 @@ def test_host_argument_checks_return_before_any_device_call():
     assert lib.mlora_pool_destroy(None) == 0
     assert lib.mlora_token_map(None, None, 0, 0, None, None, None) == 0      # zero tokens: no-op
     assert lib.mlora_token_map(None, None, 4, 1, None, None, None) == E["MLORA_ERR_INVALID_ARG"]
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # the layer is built and measured on one GPU: bench.py says so and exits
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
