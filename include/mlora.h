@@ -178,7 +178,11 @@ int mlora_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t st
  * n_seg: 1 .. MLORA_MAX_SEGMENTS when lora_on = 1.
  * Errors: MLORA_ERR_INVALID_ARG, MLORA_ERR_SHAPE, MLORA_ERR_WORKSPACE,
  * MLORA_ERR_METADATA (n_seg < 1) from host checks. Inconsistent device
- * metadata is not detected here (see mlora_validate). */
+ * metadata is not detected here (see mlora_validate), unless the environment
+ * sets MLORA_DEBUG_VALIDATE=1: then the call first checks the metadata on
+ * the device as mlora_validate does (synchronizing `stream`) and returns
+ * MLORA_ERR_METADATA, MLORA_ERR_ADAPTER or MLORA_ERR_RANK without running
+ * the layer (also for mlora_linear_fp8w). */
 int mlora_linear(const void* x, const void* W, mlora_pool_t pool, const int32_t* seg_start,
                  const int32_t* seg_adapter, const int32_t* seg_rank, const float* seg_scale,
                  const int32_t* token_index, int n_tokens, int n_seg, int lora_on, void* y,

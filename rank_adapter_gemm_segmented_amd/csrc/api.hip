@@ -119,6 +119,14 @@ int forced_path() {
 
 int check_launch() { return hip_status(hipGetLastError()); }
 
+// MLORA_DEBUG_VALIDATE=1: the layer entry points check sorted metadata on the
+// device first (as mlora_validate, which synchronizes the stream) and return
+// its error instead of running the layer.
+bool debug_validate() {
+  const char* e = getenv("MLORA_DEBUG_VALIDATE");
+  return e && e[0] == '1' && e[1] == 0;
+}
+
 // Launch the layer on sorted metadata already resident on the device.
 // w_scale != null: W holds FP8 e4m3 codes with a float32 scale per row (bf16
 // pool, split-K decode path only; the caller has checked the shape).
@@ -394,6 +402,11 @@ int mlora_linear(const void* x, const void* W, mlora_pool_t pool, const int32_t*
     sv.token_index = token_index;
     sv.n_seg_dev = nullptr;
     sv.n_seg = n_seg;
+    if (debug_validate()) {
+      const int st = mlora_validate(pool, seg_start, seg_adapter, seg_rank, token_index, n_tokens, n_seg,
+                                    workspace, workspace_bytes, stream);
+      if (st != MLORA_OK) return st;
+    }
   }
   return run_linear(x, W, pool, sv, n_tokens, lora_on, y, (char*)workspace, stream);
 }
@@ -428,6 +441,11 @@ int mlora_linear_fp8w(const void* x, const uint8_t* W_fp8, const float* w_scale,
   }
   if (!decode_supported(n_tokens, lora_on ? n_seg : 0, pool->d_out, pool->max_rank))
     return MLORA_ERR_SHAPE;
+  if (lora_on && debug_validate()) {
+    const int st = mlora_validate(pool, seg_start, seg_adapter, seg_rank, token_index, n_tokens, n_seg,
+                                  workspace, workspace_bytes, stream);
+    if (st != MLORA_OK) return st;
+  }
   return run_linear(x, W_fp8, pool, sv, n_tokens, lora_on, y, (char*)workspace, stream, w_scale);
 }
 

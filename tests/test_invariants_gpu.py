@@ -179,3 +179,33 @@ def test_build_segments_at_the_token_limit():
     assert np.array_equal(ss[:S + 1].cpu().numpy(), o_ss)
     assert np.array_equal(sa[:S].cpu().numpy(), o_sa)
     assert np.array_equal(sr[:S].cpu().numpy(), np.array([c.adapters[a].rank if a >= 0 else 0 for a in o_sa]))
+
+
+def test_debug_validate_mode(monkeypatch):
+    # MLORA_DEBUG_VALIDATE=1: bad metadata is reported by the layer call itself
+    # (and nothing is written); good metadata gives the ordinary result
+    log("[invariant] MLORA_DEBUG_VALIDATE")
+    ml = _ml()
+    E = ml.STATUS_CODE
+    ids = sorted(np.random.default_rng(9).integers(0, 4, size=24).tolist())
+    c = make_custom_case(91, "bf16", 256, 192, ids, {a: 8 for a in range(4)})
+    dc = DeviceCase(c)
+    y_plain = dc.run(1).clone()
+    monkeypatch.setenv("MLORA_DEBUG_VALIDATE", "1")
+    assert torch.equal(dc.run(1).view(torch.int16), y_plain.view(torch.int16))
+    bad = [
+        ("seg_start ends short", dict(seg_start=np.r_[c.seg_start[:-1], c.seg_start[-1] - 1]), "MLORA_ERR_METADATA"),
+        ("unregistered adapter", dict(seg_adapter=np.where(c.seg_adapter == 2, 7, c.seg_adapter)), "MLORA_ERR_ADAPTER"),
+        ("rank mismatch", dict(seg_rank=c.seg_rank + 8), "MLORA_ERR_RANK"),
+    ]
+    for what, change, code in bad:
+        meta = dict(seg_start=c.seg_start, seg_adapter=c.seg_adapter, seg_rank=c.seg_rank)
+        meta.update(change)
+        y = torch.full_like(y_plain, 7.0)
+        with pytest.raises(ml.MloraError) as e:
+            ml.linear(dc.x, dc.W, dc.pool, i32(meta["seg_start"]), i32(meta["seg_adapter"]),
+                      i32(meta["seg_rank"]), f32(c.seg_scale), lora_on=1, out=y, workspace=dc.ws)
+        assert e.value.code == E[code], what
+        torch.cuda.synchronize()
+        assert bool((y == 7.0).all()), f"{what}: the layer ran"
+    monkeypatch.delenv("MLORA_DEBUG_VALIDATE")
