@@ -209,3 +209,18 @@ def test_debug_validate_mode(monkeypatch):
         torch.cuda.synchronize()
         assert bool((y == 7.0).all()), f"{what}: the layer ran"
     monkeypatch.delenv("MLORA_DEBUG_VALIDATE")
+
+
+def test_log_mode(monkeypatch, capfd):
+    # MLORA_LOG=1: one stderr line per call naming the path taken
+    log("[invariant] MLORA_LOG")
+    ml = _ml()
+    monkeypatch.setenv("MLORA_LOG", "1")
+    for T, path in ((16, "path=decode "), (200, "path=gemm ")):
+        ids = sorted(np.random.default_rng(T).integers(0, 4, size=T).tolist())
+        dc = DeviceCase(make_custom_case(92, "bf16", 256, 192, ids, {a: 8 for a in range(4)}))
+        capfd.readouterr()
+        dc.run(1)
+        err = capfd.readouterr().err
+        assert path in err and f"T={T} " in err and "lora_on=1" in err, err
+    monkeypatch.delenv("MLORA_LOG")
