@@ -22,6 +22,9 @@
 // column l%32. The A operand is W (rows = output features) and the B operand
 // is x (columns = tokens), so each lane ends with runs of 4 consecutive
 // features of one token.
+#include <cstdlib>
+#include <cstring>
+
 #include "common.h"
 #include "launch.h"
 
@@ -258,6 +261,202 @@ __global__ __launch_bounds__(256) void k_shrink2(LinearArgs a) {
     }
   }
   write_pos();
+}
+
+// ---------------------------------------------------------------------------
+// Shrink for batches of short segments (a verify batch: a draft and a bonus
+// token per request, each request with its own adapter), one d_in chunk.
+// The MFMA shrink above spends most of its loads there on absent positions
+// (a 16-position operand for one or two tokens). Here grid.y is the item, a
+// block of up to kSsPos positions of one segment, and grid.x a group of
+// kSsRows rank rows, so only real A rows and real tokens are read, and a
+// rank-16 adapter's A is shared by two workgroups. Thread tid takes the 8-column
+// groups tid, tid + 256, ... of d_in and accumulates kSsRows x kSsPos fp32
+// dot products on the vector ALUs; the 256 threads' sums are then added
+// through LDS in a fixed order (deterministic). Writes v_fin = scale * v and
+// the position table, as the one-chunk MFMA shrink does.
+// ---------------------------------------------------------------------------
+constexpr int kSsPos = 4;      // positions per item
+constexpr int kSsRows = 8;     // rank rows per workgroup (4 measured the same, 16 slower)
+constexpr int kSsUnroll = 2;   // column groups per thread whose loads are in flight together
+constexpr int kSsPitch = 256 + 8;
+
+__device__ __forceinline__ float dot8_bf16(u32x4_t a, u32x4_t b, float acc) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc = fmaf(__uint_as_float(a[i] << 16), __uint_as_float(b[i] << 16), acc);
+    acc = fmaf(__uint_as_float(a[i] & 0xffff0000u), __uint_as_float(b[i] & 0xffff0000u), acc);
+  }
+  return acc;
+}
+
+__global__ __launch_bounds__(256) void k_shrink_short(LinearArgs a) {
+  // rank groups vary fastest, so the workgroups of real items come first and
+  // spread one per CU
+  const int g = blockIdx.x, item = blockIdx.y;
+  const SegView& sv = a.sv;
+  const int S = min(seg_count(sv), kShrMaxSeg);
+  const int T = a.T, d_in = a.d_in;
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave, lane = tid % kWave;
+  extern __shared__ int sdyn[];
+  const bool meta_lds = S <= kShrLdsSeg;
+  int* sst = sdyn;
+  int* sad = sdyn + S + 1;
+  int* srk = sdyn + 2 * S + 1;
+  __shared__ int wsum[4];
+  __shared__ int found[2];
+  __shared__ float red[kSsRows * kSsPos][kSsPitch];
+
+  // ---- which (segment, block) is this item? (as in k_shrink2, blocks of kSsPos)
+  for (int i0 = 0; i0 <= S; i0 += 256) {
+    const int i = i0 + tid;
+    const bool in = i <= S, meta = meta_lds && i < S;
+    const int st = in ? sv.seg_start[i] : 0;
+    const int ad = meta ? sv.seg_adapter[i] : 0;
+    const int rk = meta && sv.seg_rank ? sv.seg_rank[i] : 0;
+    if (in) sst[i] = st;
+    if (meta) {
+      sad[i] = ad;
+      srk[i] = rk;
+    }
+  }
+  if (tid == 0) found[0] = -1;
+  __syncthreads();
+  const int per = (S + 255) / 256;
+  int cnt = 0;
+  for (int i = tid * per; i < min(S, tid * per + per); ++i) {
+    const int len = min(sst[i + 1], T) - max(sst[i], 0);
+    cnt += len > 0 ? (len + kSsPos - 1) / kSsPos : 0;
+  }
+  int inc = cnt;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int up = __shfl_up(inc, off, kWave);
+    if (lane >= off) inc += up;
+  }
+  if (lane == kWave - 1) wsum[wave] = inc;
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) inc += wsum[w];
+  {
+    const int lo = inc - cnt;
+    if (item >= lo && item < inc) {
+      int acc = lo;
+      for (int i = tid * per; i < min(S, tid * per + per); ++i) {
+        const int len = min(sst[i + 1], T) - max(sst[i], 0);
+        const int nb = len > 0 ? (len + kSsPos - 1) / kSsPos : 0;
+        if (item < acc + nb) {
+          found[0] = i;
+          found[1] = item - acc;
+          break;
+        }
+        acc += nb;
+      }
+    }
+  }
+  __syncthreads();
+  const int s = found[0];
+  if (s < 0) return;   // uniform: past the last item
+  const int ps = max(sst[s], 0) + kSsPos * found[1];
+  const int pe = min(min(sst[s + 1], T), ps + kSsPos);
+  const int np = pe - ps;
+  const int ad0 = meta_lds ? sad[s] : sv.seg_adapter[s];
+  const int rk0 = meta_lds ? srk[s] : (sv.seg_rank ? sv.seg_rank[s] : 0);
+  const bool adok = ad0 >= 0 && ad0 < a.pv.capacity;
+  const int ra = adok ? min(max(rk0, 0), a.pv.max_rank) : 0;
+  const int j0 = kSsRows * g;
+  const int nr = min(kSsRows, ra - j0);   // rows of this workgroup (<= 0: none)
+
+  const uint16_t* __restrict__ x = (const uint16_t*)a.x;
+  const uint16_t* __restrict__ Aa = (const uint16_t*)a.pv.base + (long long)(adok ? ad0 : 0) * a.pv.slot_elems;
+  const uint16_t* arow[kSsRows];
+#pragma unroll
+  for (int r = 0; r < kSsRows; ++r) arow[r] = Aa + (long long)(j0 + min(r, max(nr - 1, 0))) * d_in;
+  int prow[kSsPos];
+#pragma unroll
+  for (int t = 0; t < kSsPos; ++t) prow[t] = min(ps + t, pe - 1);
+  if (sv.token_index) {   // uniform
+#pragma unroll
+    for (int t = 0; t < kSsPos; ++t) prow[t] = sv.token_index[prow[t]];
+  }
+  const uint16_t* xrow[kSsPos];
+#pragma unroll
+  for (int t = 0; t < kSsPos; ++t) xrow[t] = x + (long long)min(max(prow[t], 0), T - 1) * d_in;
+  // the registered rank and the scale are needed at the end only: vector
+  // loads (offset vz is zero but held in a vector register), consumed after
+  // the dot products, so the A and x loads do not wait behind them
+  int vz;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(vz));
+  int reg_rank = a.pv.rank[(adok ? ad0 : 0) + vz];
+  float scl = sv.seg_scale[s + vz];
+  // position table and v_fin columns [ra, r_ws) of the item's positions
+  auto write_pos = [&]() {
+    asm volatile("" : "+v"(reg_rank), "+v"(scl));
+    const int r_eff = adok && reg_rank > 0 && ra > 0 ? min(ra, reg_rank) : 0;
+    if (g != 0) return r_eff;
+    const int ad = r_eff > 0 ? ad0 : -1;
+    for (int p = ps + tid; p < pe; p += 256) a.pos_info[p] = make_int4(s, ad, r_eff, __float_as_int(r_eff > 0 ? scl : 0.f));
+    const int nz = a.r_ws - ra;
+    for (int e = tid; e < np * nz; e += 256) a.v_fin[(long long)(ps + e / nz) * a.r_ws + ra + e % nz] = 0.f;
+    return r_eff;
+  };
+  if (nr <= 0) {   // uniform
+    write_pos();
+    return;
+  }
+
+  // ---- dot products over the thread's column groups --------------------------
+  float acc[kSsRows][kSsPos];
+#pragma unroll
+  for (int r = 0; r < kSsRows; ++r)
+#pragma unroll
+    for (int t = 0; t < kSsPos; ++t) acc[r][t] = 0.f;
+  const int ncg = d_in / 8;
+  for (int cg0 = tid; cg0 < ncg; cg0 += 256 * kSsUnroll) {
+    u32x4_t av[kSsUnroll][kSsRows], xv[kSsUnroll][kSsPos];
+#pragma unroll
+    for (int u = 0; u < kSsUnroll; ++u) {
+      const int cg = cg0 + 256 * u;
+      const int col = 8 * (cg < ncg ? cg : cg0);
+#pragma unroll
+      for (int r = 0; r < kSsRows; ++r) av[u][r] = r < nr ? ld16(arow[r] + col) : zero_u32x4();
+#pragma unroll
+      for (int t = 0; t < kSsPos; ++t) xv[u][t] = t < np ? ld16(xrow[t] + col) : zero_u32x4();
+    }
+#pragma unroll
+    for (int u = 0; u < kSsUnroll; ++u)
+      if (cg0 + 256 * u < ncg) {
+#pragma unroll
+        for (int r = 0; r < kSsRows; ++r)
+#pragma unroll
+          for (int t = 0; t < kSsPos; ++t) acc[r][t] = dot8_bf16(av[u][r], xv[u][t], acc[r][t]);
+      }
+  }
+
+  // ---- fixed-order sum over the 256 threads -----------------------------------
+  // output o = r * kSsPos + t; TPO threads per output each add 256 / TPO
+  // partials (columns q, q + TPO, ...), then the TPO sums are combined by a
+  // shuffle tree
+  constexpr int NO = kSsRows * kSsPos;
+  constexpr int TPO = 256 / NO;
+  static_assert(NO * TPO == 256 && TPO >= 1 && TPO <= kWave, "outputs must divide the workgroup");
+#pragma unroll
+  for (int r = 0; r < kSsRows; ++r)
+#pragma unroll
+    for (int t = 0; t < kSsPos; ++t) red[r * kSsPos + t][tid] = acc[r][t];
+  __syncthreads();
+  const int o = tid / TPO, q = tid % TPO;
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 256 / TPO; ++i) sum += red[o][q + TPO * i];
+#pragma unroll
+  for (int off = 1; off < TPO; off <<= 1) sum += __shfl_xor(sum, off, TPO);
+  const int r_eff = write_pos();
+  const int r = o / kSsPos, t = o % kSsPos;
+  if (q == 0 && r < nr && t < np) {
+    const int j = j0 + r;
+    a.v_fin[(long long)(ps + t) * a.r_ws + j] = j < r_eff ? scl * sum : 0.f;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -799,6 +998,22 @@ static void launch_g(const LinearArgs& a, hipStream_t st) {
                      dim3(GCfg<BR, BT, WR, WT, NB, KB, DMA>::NT), 0, st, a);
 }
 
+// MLORA_FORCE_SHRINK=mfma keeps the MFMA shrink on short segments too.
+static bool shrink_short_enabled() {
+  const char* e = getenv("MLORA_FORCE_SHRINK");
+  return !(e && strcmp(e, "mfma") == 0);
+}
+
+// The vector-ALU shrink for short segments: a segment count known on the
+// host with at most two positions per segment on average, and ranks up to 16
+// (its items re-read an adapter's A for every kSsPos positions of a longer
+// segment), one d_in chunk. Segments built on the device only bound their
+// count by T, so they keep the MFMA shrink.
+bool shrink_short(const LinearArgs& a) {
+  return a.lora_on && a.ks == 1 && a.sv.n_seg_dev == nullptr && a.seg_grid > 0 && a.T <= 2 * a.seg_grid &&
+         a.pv.max_rank <= 16 && shrink_short_enabled();
+}
+
 // Tile choice: large batches take 256x256 tiles (MFMA-bound, ~30 B/clk of L2
 // per CU); otherwise a tile spans every position of the batch (one read of x
 // per CU) with as few W rows as keep the CUs busy.
@@ -811,6 +1026,12 @@ void launch_shrink_bf16(const LinearArgs& a, hipStream_t st) {
     const bool long_segs = a.T > 16 * a.seg_grid;
     const dim3 grid(shrink_items_bound(a.T, a.seg_grid), a.ks);
     const size_t lds = (size_t)(nseg <= kShrLdsSeg ? 3 * nseg + 1 : nseg + 1) * sizeof(int);
+    if (shrink_short(a)) {
+      // at most two positions per segment on average, one d_in chunk, ranks <= 16
+      const dim3 gs((a.pv.max_rank + kSsRows - 1) / kSsRows, nseg + (a.T + kSsPos - 1) / kSsPos);
+      hipLaunchKernelGGL(k_shrink_short, gs, dim3(256), lds, st, a);
+      return;
+    }
     if (long_segs) {
       if (rmax <= 16) hipLaunchKernelGGL((k_shrink2<4, 1>), grid, dim3(256), lds, st, a);
       else if (rmax <= 32) hipLaunchKernelGGL((k_shrink2<4, 2>), grid, dim3(256), lds, st, a);

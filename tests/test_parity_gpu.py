@@ -255,3 +255,50 @@ def test_wide_layer_path_switch(T):
     dc = DeviceCase(c)
     check_case(dc, 1, what=f"wide T={T} lora_on=1")
     check_case(dc, 0, what=f"wide T={T} lora_on=0")
+
+
+def _short_segment_ids(seed, n_seg, n_ad):
+    # runs of 1-3 positions, a few of 5-9 (several items of one segment),
+    # some base-only runs (id -1); at most two positions per segment on average
+    rng = np.random.default_rng(seed)
+    ids = []
+    for s in range(n_seg):
+        n = int(rng.choice([1, 1, 2, 2, 2, 3])) if s % 23 else int(rng.integers(5, 10))
+        ids += [int(rng.integers(-1, n_ad))] * n
+    return ids
+
+
+@pytest.mark.parametrize("shrink", ["short", "mfma"])
+def test_short_segment_shrink(shrink, monkeypatch):
+    # a verify-shaped batch (T > 64, T <= 2 * segments, ranks <= 16) takes the
+    # vector-ALU shrink; MLORA_FORCE_SHRINK=mfma keeps the MFMA one. Ranks 4 and
+    # 12 leave partial 8-row groups; d_in = 4104 leaves a column-group tail.
+    if shrink == "mfma":
+        monkeypatch.setenv("MLORA_FORCE_SHRINK", "mfma")
+    ids = _short_segment_ids(120, 90, 40)
+    T = len(ids)
+    n_seg = 1 + sum(1 for i in range(1, T) if ids[i] != ids[i - 1])
+    assert 64 < T <= 2 * n_seg, (T, n_seg)
+    ranks = {a: [4, 8, 12, 16][a % 4] for a in range(40)}
+    log(f"[parity] short segments ({shrink} shrink): 4104->300, T={T}, {n_seg} segments")
+    c = make_custom_case(120, "bf16", 4104, 300, ids, ranks)
+    dc = DeviceCase(c)
+    check_case(dc, 1, what=f"short segments {shrink} lora_on=1")
+    check_case(dc, 0, what=f"short segments {shrink} lora_on=0")
+
+
+def test_short_segment_shrink_verify_shape():
+    # the verify batch (128 requests x 2 tokens, 128 rank-16 adapters): the
+    # two shrinks agree with each other within the bf16 tolerance on every row
+    import rank_adapter_gemm_segmented_amd as ml  # noqa: F401
+    import os
+    dc = _dev("verify_bf16")
+    y_short = y_host(dc.run(1)).astype(np.float64)
+    os.environ["MLORA_FORCE_SHRINK"] = "mfma"
+    try:
+        y_mfma = y_host(dc.run(1)).astype(np.float64)
+    finally:
+        del os.environ["MLORA_FORCE_SHRINK"]
+    worst = float(np.max(np.abs(y_short - y_mfma) / (2e-2 * (1 + np.abs(y_mfma)))))
+    log(f"  verify short vs mfma shrink: max diff/bound {worst:.3f}")
+    assert worst <= 1.0
