@@ -208,7 +208,12 @@ def layer_kernels(case):
     if case.dtype == "bf16" and case.n_tokens <= 64 and not wide:
         return ["k_stream_bf16", "k_finish_bf16"]
     if case.dtype == "bf16":
-        return ((["k_build_segments"] if not case.sorted_input else []) + ["k_shrink2"] +
+        # the vector-ALU shrink on host-known short segments (kernels_gemm.hip,
+        # shrink_short): at most two positions per segment, ranks <= 16
+        short = (case.sorted_input and case.n_tokens <= 2 * case.n_seg and case.max_rank <= 16 and
+                 shrink_split(case) == 1 and os.environ.get("MLORA_FORCE_SHRINK") != "mfma")
+        return ((["k_build_segments"] if not case.sorted_input else []) +
+                (["k_shrink_short"] if short else ["k_shrink2"]) +
                 (["k_vfinal"] if shrink_split(case) > 1 else []) + ["k_gemm2"])
     return ["k_shrink_f32", "k_gemm_f32"]
 
