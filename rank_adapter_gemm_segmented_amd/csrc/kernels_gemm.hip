@@ -24,6 +24,7 @@
 // features of one token.
 #include <cstdlib>
 #include <cstring>
+#include <type_traits>
 
 #include "common.h"
 #include "launch.h"
@@ -46,10 +47,12 @@ __device__ __forceinline__ f32x16_t mfma32g(u32x4_t a, u32x4_t b, f32x16_t c) {
 // start right after the scan (the pool's slot table is read alongside and
 // only decides the per-position table). Chunk c covers k-steps
 // [c*nks/ks, (c+1)*nks/ks) of 32; wave w takes every fourth k-step starting
-// at w, with a ring of D k-steps of operands in flight in registers. A
-// k-step loads NRB position blocks of x and NCB rank blocks of A (16 each):
-// the kernel is instantiated for the block counts the batch needs, so a
-// short, low-rank segment keeps a deep ring of useful loads. Absent operands
+// at w. A k-step loads NRB position blocks of x and NC rank blocks of A (16
+// each). The kernel is instantiated for the batch's position-block count and
+// its pool's largest rank (NCB blocks); each pass over a segment's rank rows
+// then takes the fewest blocks NC <= NCB that hold them, so a short, low-rank
+// segment keeps a deep ring of useful loads: 16 / (NRB + NC) k-steps of
+// operands in flight in registers (at most 64 operand VGPRs). Absent operands
 // read the pool's zero block (every load is unconditional, no loaded value
 // is selected). The four waves are summed in a fixed order through LDS into
 // v_part[c][p][j] (unscaled). MFMA rows = positions, columns = rank index.
@@ -59,7 +62,6 @@ constexpr int kShrLdsSeg = 4096;                // up to this many, adapters and
 
 template <int NRB, int NCB>
 __global__ __launch_bounds__(256) void k_shrink2(LinearArgs a) {
-  constexpr int D = 16 / (NRB + NCB);   // k-steps in flight per wave (<= 64 operand VGPRs)
   constexpr int NQ = NRB * NCB * 4;     // accumulator floats per lane
   const int item = blockIdx.x, c = blockIdx.y;
   const SegView& sv = a.sv;
@@ -178,7 +180,6 @@ __global__ __launch_bounds__(256) void k_shrink2(LinearArgs a) {
   const int ke = (int)((long long)(c + 1) * nks / a.ks);
   const int nst = (ke - kb - wave + 3) / 4;            // this wave's k-steps
   const int nst_w = (ke - kb + 3) / 4;                 // wave 0's (the most); uniform loop bound
-  const int nst_pad = (nst_w + D - 1) / D * D;
   const int l16 = lane % 16, kq = 8 * (lane / 16);
 
   for (int pg = ps; pg < pe; pg += 16 * NRB) {
@@ -200,64 +201,87 @@ __global__ __launch_bounds__(256) void k_shrink2(LinearArgs a) {
     }
     const int nrb = min(NRB, (pe - pg + 15) / 16);
     for (int jg = 0; jg < ra; jg += 16 * NCB) {
-      const uint16_t* arow[NCB];
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        const int j = jg + cb * 16 + l16;
-        arow[cb] = j < ra ? Aa + (long long)j * d_in : nullptr;
-      }
       const int ncb = min(NCB, (ra - jg + 15) / 16);
-      f32x4_t acc[NRB][NCB];
+      // one pass over rank columns [jg, jg + 16 NC): NC column blocks of 16
+      // A rows are loaded per k-step. The pass takes the smallest NC that
+      // holds the segment's rows, so a low-rank segment in a pool of a high
+      // max rank loads no zero blocks for its absent rows and keeps a deeper
+      // ring (DD k-steps in flight).
+      auto pass = [&](auto nc_tag) {
+        constexpr int NC = decltype(nc_tag)::value;
+        constexpr int DD = 16 / (NRB + NC);
+        const int nst_pd = (nst_w + DD - 1) / DD * DD;
+        const uint16_t* arow[NC];
 #pragma unroll
-      for (int rb = 0; rb < NRB; ++rb)
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) acc[rb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      u32x4_t af[D][NCB], xf[D][NRB];
-      auto load = [&](int slot, int i) {   // this wave's i-th k-step
-        const int k = (kb + wave + 4 * i) * 32 + kq;
-        const bool kin = i < nst && k < d_in;
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) af[slot][cb] = ld16(kin && arow[cb] ? arow[cb] + k : zeros + kq);
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) xf[slot][rb] = ld16(kin && xrow[rb] ? xrow[rb] + k : zeros + kq);
-      };
-#pragma unroll
-      for (int u = 0; u < D; ++u) load(u, u);
-      for (int i0 = 0; i0 < nst_pad; i0 += D) {
-#pragma unroll
-        for (int u = 0; u < D; ++u) {
-#pragma unroll
-          for (int rb = 0; rb < NRB; ++rb)
-#pragma unroll
-            for (int cb = 0; cb < NCB; ++cb)
-              if (rb < nrb && cb < ncb) acc[rb][cb] = mfma16g(xf[u][rb], af[u][cb], acc[rb][cb]);
-          load(u, i0 + u + D);   // past the end: zero-block reads
+        for (int cb = 0; cb < NC; ++cb) {
+          const int j = jg + cb * 16 + l16;
+          arow[cb] = j < ra ? Aa + (long long)j * d_in : nullptr;
         }
-      }
-      resolve();
-      // fixed-order sum of the four waves, spread over all threads: entry
-      // e = (q, l) is accumulator value q of lane l
+        f32x4_t acc[NRB][NC];
 #pragma unroll
-      for (int rb = 0; rb < NRB; ++rb)
+        for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb)
+          for (int cb = 0; cb < NC; ++cb) acc[rb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        u32x4_t af[DD][NC], xf[DD][NRB];
+        auto load = [&](int slot, int i) {   // this wave's i-th k-step
+          const int k = (kb + wave + 4 * i) * 32 + kq;
+          const bool kin = i < nst && k < d_in;
 #pragma unroll
-          for (int v = 0; v < 4; ++v) red[wave][lane][(rb * NCB + cb) * 4 + v] = acc[rb][cb][v];
-      __syncthreads();
-      for (int e = tid; e < NQ * kWave; e += 256) {
-        const int q = e / kWave, l = e % kWave;
-        const int rb = q / (NCB * 4), cb = (q / 4) % NCB, v = q % 4;
-        if (rb < nrb && cb < ncb) {
-          const float sum = ((red[0][l][q] + red[1][l][q]) + red[2][l][q]) + red[3][l][q];
-          const int p = pg + rb * 16 + 4 * (l / 16) + v;
-          const int j = jg + cb * 16 + (l % 16);
-          if (p < pe && j < ra) {
-            if (fused) a.v_fin[(long long)p * a.r_ws + j] = j < r_eff ? scl * sum : 0.f;
-            else a.v_part[((long long)c * T + p) * a.r_ws + j] = sum;
+          for (int cb = 0; cb < NC; ++cb) af[slot][cb] = ld16(kin && arow[cb] ? arow[cb] + k : zeros + kq);
+#pragma unroll
+          for (int rb = 0; rb < NRB; ++rb) xf[slot][rb] = ld16(kin && xrow[rb] ? xrow[rb] + k : zeros + kq);
+        };
+#pragma unroll
+        for (int u = 0; u < DD; ++u) load(u, u);
+        for (int i0 = 0; i0 < nst_pd; i0 += DD) {
+#pragma unroll
+          for (int u = 0; u < DD; ++u) {
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+              for (int cb = 0; cb < NC; ++cb)
+                if (rb < nrb && cb < ncb) acc[rb][cb] = mfma16g(xf[u][rb], af[u][cb], acc[rb][cb]);
+            load(u, i0 + u + DD);   // past the end: zero-block reads
           }
         }
+        resolve();
+        // fixed-order sum of the four waves, spread over all threads: entry
+        // e = (q, l) is accumulator value q of lane l
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+          for (int cb = 0; cb < NC; ++cb)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) red[wave][lane][(rb * NC + cb) * 4 + v] = acc[rb][cb][v];
+        __syncthreads();
+        for (int e = tid; e < NRB * NC * 4 * kWave; e += 256) {
+          const int q = e / kWave, l = e % kWave;
+          const int rb = q / (NC * 4), cb = (q / 4) % NC, v = q % 4;
+          if (rb < nrb && cb < ncb) {
+            const float sum = ((red[0][l][q] + red[1][l][q]) + red[2][l][q]) + red[3][l][q];
+            const int p = pg + rb * 16 + 4 * (l / 16) + v;
+            const int j = jg + cb * 16 + (l % 16);
+            if (p < pe && j < ra) {
+              if (fused) a.v_fin[(long long)p * a.r_ws + j] = j < r_eff ? scl * sum : 0.f;
+              else a.v_part[((long long)c * T + p) * a.r_ws + j] = sum;
+            }
+          }
+        }
+        __syncthreads();
+      };
+      if constexpr (NCB >= 2) {
+        if (ncb == 1) {   // uniform
+          pass(std::integral_constant<int, 1>{});
+          continue;
+        }
       }
-      __syncthreads();
+      if constexpr (NCB >= 4) {
+        if (ncb == 2) {
+          pass(std::integral_constant<int, 2>{});
+          continue;
+        }
+      }
+      pass(std::integral_constant<int, NCB>{});
     }
   }
   write_pos();
