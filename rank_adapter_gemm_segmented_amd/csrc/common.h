@@ -60,6 +60,14 @@ __device__ __forceinline__ int find_segment(const int32_t* __restrict__ seg_star
 
 __device__ __forceinline__ int round_up8(int r) { return (r + 7) & ~7; }
 
+// Workgroup barrier for LDS data only: waits for this wave's LDS (and scalar)
+// operations, not for its outstanding global loads, which __syncthreads
+// would wait for too. The memory clobber keeps the compiler from moving
+// memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 constexpr int kZeroBlockElems = 2048;   // bf16 elements in the pool's zero block (4 KB)
 
 // Everything a kernel needs to find an adapter in the pool.

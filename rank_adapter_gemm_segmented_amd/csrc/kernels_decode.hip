@@ -51,13 +51,6 @@ __device__ __forceinline__ long long part_off(int c, int i, int rb, int tb, int 
   return ((((long long)c * n_tiles + i) * 4 + rb) * ntb + tb) * 256;
 }
 
-// Workgroup barrier for LDS data only: waits for this wave's LDS (and scalar)
-// operations, not for its outstanding global loads, which __syncthreads
-// would wait for too. The memory clobber keeps the compiler from moving
-// memory accesses across it.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 // Eight FP8 e4m3 codes (OCP E4M3: bias 7, subnormals m/8 * 2^-6) -> eight
 // bf16 values, exact: every e4m3 value has at most 4 significant bits and an

@@ -50,7 +50,9 @@ void launch_token_map(const int32_t* seg_start, const int32_t* seg_adapter, int 
 //
 // Latency: every global load happens up front (ids, then each token's
 // registered rank and scale); the sort, the segment flags and the scan stay in
-// LDS (one wave-level scan, one cross-wave step).
+// LDS (one wave-level scan, one cross-wave step). The rank and scale loads stay
+// in flight through the stable count (its barrier waits for LDS only) and land
+// in LDS just before the segment phase, which is their first use.
 // ---------------------------------------------------------------------------
 constexpr int kSegThreads = 1024;
 constexpr int kSegPerThread = MLORA_MAX_UNSORTED_TOKENS / kSegThreads;   // tokens per thread (8)
@@ -77,19 +79,17 @@ __global__ __launch_bounds__(kSegThreads) void k_build_segments(
     const int t = tid + kSegThreads * i;
     key[i] = t < T ? token_adapter[t] : -1;
   }
+  int rk[kSegPerThread];
+  float sc[kSegPerThread];
 #pragma unroll
   for (int i = 0; i < kSegPerThread; ++i) {
     const int t = tid + kSegThreads * i;
     const bool valid = key[i] >= 0 && key[i] < pv.capacity;
-    const int r = valid ? pv.rank[key[i]] : 0;
-    const float sc = valid ? adapter_scale[key[i]] : 0.0f;
-    if (t < T) {
-      ids[t] = key[i];
-      trk[t] = r;
-      tsc[t] = sc;
-    }
+    rk[i] = valid ? pv.rank[key[i]] : 0;
+    sc[i] = valid ? adapter_scale[key[i]] : 0.0f;
+    if (t < T) ids[t] = key[i];
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- stable rank of every token: G threads share one token's count -------
   int G = 1;
@@ -107,6 +107,14 @@ __global__ __launch_bounds__(kSegThreads) void k_build_segments(
     if (t < T && sub == 0) {
       srt[pos] = t;
       token_index[pos] = t;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kSegPerThread; ++i) {
+    const int t = tid + kSegThreads * i;
+    if (t < T) {
+      trk[t] = rk[i];
+      tsc[t] = sc[i];
     }
   }
   __syncthreads();
