@@ -184,8 +184,9 @@ int mlora_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t st
  * MLORA_ERR_METADATA, MLORA_ERR_ADAPTER or MLORA_ERR_RANK without running
  * the layer (also for mlora_linear_fp8w). With MLORA_LOG=1 every layer call
  * prints one line on stderr: the path taken (decode, decode-fp8w, gemm, gemv,
- * f32), T, the shape, dtype, lora_on, the segment count, the d_in split and
- * the pool's max rank. */
+ * f32), T, the shape, dtype, lora_on, the segment count, the d_in split,
+ * the shrink kernel (short, mfma, fused into the decode stream, f32 or none)
+ * and the pool's max rank. */
 int mlora_linear(const void* x, const void* W, mlora_pool_t pool, const int32_t* seg_start,
                  const int32_t* seg_adapter, const int32_t* seg_rank, const float* seg_scale,
                  const int32_t* token_index, int n_tokens, int n_seg, int lora_on, void* y,

@@ -126,10 +126,12 @@ bool log_calls() {
   return e && e[0] == '1' && e[1] == 0;
 }
 
-void log_call(const char* path, int T, const mlora_pool_s* p, const SegView& sv, int lora_on, int ks) {
-  fprintf(stderr, "mlora: path=%s T=%d d_in=%d d_out=%d dtype=%s lora_on=%d segments=%d%s ks=%d max_rank=%d\n",
+void log_call(const char* path, int T, const mlora_pool_s* p, const SegView& sv, int lora_on, int ks,
+              const char* shrink = "none") {
+  fprintf(stderr,
+          "mlora: path=%s T=%d d_in=%d d_out=%d dtype=%s lora_on=%d segments=%d%s ks=%d shrink=%s max_rank=%d\n",
           path, T, p->d_in, p->d_out, p->dtype == MLORA_BF16 ? "bf16" : "f32", lora_on, lora_on ? sv.n_seg : 0,
-          sv.n_seg_dev ? "(bound)" : "", ks, p->max_rank);
+          sv.n_seg_dev ? "(bound)" : "", ks, shrink, p->max_rank);
 }
 
 // MLORA_DEBUG_VALIDATE=1: the layer entry points check sorted metadata on the
@@ -186,7 +188,8 @@ int run_linear(const void* x, const void* W, mlora_pool_s* pool, const SegView& 
       decode_plan(pool->d_in, pool->d_out, &d.n_tiles, &d.kc, &d.n_chunks);
       d.unit_rows = decode_unit_rows(lora_on ? sv.n_seg : 0, pool->max_rank, d.n_tiles);
       d.w_scale = w_scale;
-      if (log_calls()) log_call(w_scale ? "decode-fp8w" : "decode", T, pool, sv, lora_on, d.n_chunks);
+      if (log_calls())
+        log_call(w_scale ? "decode-fp8w" : "decode", T, pool, sv, lora_on, d.n_chunks, lora_on ? "fused" : "none");
       launch_decode_bf16(d, stream);
       return check_launch();
     }
@@ -196,16 +199,18 @@ int run_linear(const void* x, const void* W, mlora_pool_s* pool, const SegView& 
     const bool one_chunk = lora_on && T <= 16 * a.seg_grid && pool->max_rank <= 16;
     a.ks = one_chunk ? 1 : choose_shrink_split_bf16(pool->d_in, shrink_items_bound(T, a.seg_grid));
     if (fp == 3 && T <= 64) {
-      if (log_calls()) log_call("gemv", T, pool, sv, lora_on, a.ks);
+      if (log_calls())
+        log_call("gemv", T, pool, sv, lora_on, a.ks, !lora_on || a.seg_grid <= 0 ? "none" : shrink_short(a) ? "short" : "mfma");
       launch_shrink_bf16(a, stream);
       launch_gemv_bf16(a, stream);
       return check_launch();
     }
-    if (log_calls()) log_call("gemm", T, pool, sv, lora_on, a.ks);
+    if (log_calls())
+      log_call("gemm", T, pool, sv, lora_on, a.ks, !lora_on || a.seg_grid <= 0 ? "none" : shrink_short(a) ? "short" : "mfma");
     launch_linear_bf16(a, stream);
   } else {
     a.ks = 1;
-    if (log_calls()) log_call("f32", T, pool, sv, lora_on, a.ks);
+    if (log_calls()) log_call("f32", T, pool, sv, lora_on, a.ks, lora_on ? "f32" : "none");
     launch_linear_f32(a, stream);
   }
   return check_launch();

@@ -89,6 +89,8 @@ void launch_shrink_bf16(const LinearArgs& a, hipStream_t st);
 void launch_gemv_bf16(const LinearArgs& a, hipStream_t st);
 int choose_shrink_split_bf16(int d_in, int seg_grid);
 int shrink_items_bound(int T, int n_seg_bound);
+// true when the shrink of this call is k_shrink_short (else k_shrink2)
+bool shrink_short(const LinearArgs& a);
 
 // decode path (kernels_decode.hip)
 bool decode_supported(int T, int n_seg_bound, int d_out, int max_rank);
