@@ -287,18 +287,14 @@ def test_short_segment_shrink(shrink, monkeypatch):
     check_case(dc, 0, what=f"short segments {shrink} lora_on=0")
 
 
-def test_short_segment_shrink_verify_shape():
+def test_short_segment_shrink_verify_shape(monkeypatch):
     # the verify batch (128 requests x 2 tokens, 128 rank-16 adapters): the
     # two shrinks agree with each other within the bf16 tolerance on every row
-    import rank_adapter_gemm_segmented_amd as ml  # noqa: F401
-    import os
     dc = _dev("verify_bf16")
-    y_short = y_host(dc.run(1)).astype(np.float64)
-    os.environ["MLORA_FORCE_SHRINK"] = "mfma"
-    try:
-        y_mfma = y_host(dc.run(1)).astype(np.float64)
-    finally:
-        del os.environ["MLORA_FORCE_SHRINK"]
+    y_short = y_host(dc.run(1))
+    monkeypatch.setenv("MLORA_FORCE_SHRINK", "mfma")
+    y_mfma = y_host(dc.run(1))
+    monkeypatch.delenv("MLORA_FORCE_SHRINK")
     worst = float(np.max(np.abs(y_short - y_mfma) / (2e-2 * (1 + np.abs(y_mfma)))))
     log(f"  verify short vs mfma shrink: max diff/bound {worst:.3f}")
     assert worst <= 1.0
