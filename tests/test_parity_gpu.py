@@ -16,7 +16,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import (DeviceCase, check_case, compare, i32, f32, log, oracle_threads,
+from gpu_util import (BF16_TOL, DeviceCase, check_case, compare, i32, f32, log, oracle_threads,
                       sample_rows, y_host)
 from mlora_inputs import PREFILL_SHAPES, make_case, make_custom_case
 
@@ -298,3 +298,29 @@ def test_short_segment_shrink_verify_shape(monkeypatch):
     worst = float(np.max(np.abs(y_short - y_mfma) / (2e-2 * (1 + np.abs(y_mfma)))))
     log(f"  verify short vs mfma shrink: max diff/bound {worst:.3f}")
     assert worst <= 1.0
+
+
+def test_short_segment_shrink_with_token_index(capfd, monkeypatch):
+    # host-known sorted segments over gathered rows (token_index): the
+    # short-segment shrink reads x through the permutation. ~150 tokens over
+    # 100 adapters of ranks 4-16, so segments average under two positions.
+    import rank_adapter_gemm_segmented_amd as ml
+    rng = np.random.default_rng(130)
+    ids = rng.integers(-1, 100, size=150).tolist()
+    ranks = {a: [4, 8, 12, 16][a % 4] for a in range(100)}
+    cu = make_custom_case(130, "bf16", 1032, 520, ids, ranks, sorted_input=False)
+    ti, ss, sa = oracle.segment(cu.token_adapter, cu.capacity)
+    assert 64 < cu.n_tokens <= 2 * (len(ss) - 1), (cu.n_tokens, len(ss) - 1)
+    sr = np.array([ranks[a] if a >= 0 else 0 for a in sa], np.int32)
+    sc = np.array([cu.adapter_scale[a] if a >= 0 else 0 for a in sa], np.float32)
+    dc = DeviceCase(cu)
+    monkeypatch.setenv("MLORA_LOG", "1")
+    capfd.readouterr()
+    y = ml.linear(dc.x, dc.W, dc.pool, i32(ss), i32(sa), i32(sr), f32(sc), lora_on=1,
+                  token_index=i32(ti), workspace=dc.ws)
+    torch.cuda.synchronize()
+    err = capfd.readouterr().err
+    assert "shrink=short" in err, err
+    log(f"[parity] short segments with token_index: T={cu.n_tokens}, {len(ss) - 1} segments")
+    y_ref = oracle.case_linear(cu, 1, threads=oracle_threads())
+    compare(y_host(y), y_ref, BF16_TOL, "short segments with token_index")
