@@ -9,6 +9,8 @@
 //             {segment, adapter, rank, scale}; k_vfinal folds the partials in
 //             chunk order and applies the scale (v_fin, read by the epilogue).
 //             With a single chunk the shrink writes v_fin itself.
+//             k_shrink_short replaces it on batches of one- or two-position
+//             segments of rank <= 16 (vector-ALU dot products, real rows only).
 //  k_gemm2    W x as a tiled GEMM on v_mfma_f32_32x32x16_bf16: block tile of
 //             BR W rows x BT sorted positions over the whole of d_in, both
 //             operands staged through LDS (a direct-to-LDS load ring on the
@@ -1002,8 +1004,9 @@ void k_gemm2(LinearArgs a) {
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-// d_in chunks of the shrink: enough workgroups for the GPU, at most 8 (the
-// GEMM epilogue sums the partials), each chunk at least one 512-wide group.
+// d_in chunks of the shrink: enough workgroups for the GPU, at most
+// kMaxShrinkSplit (the partials k_vfinal folds), each chunk at least one
+// 512-wide group.
 int choose_shrink_split_bf16(int d_in, int items) {
   const int groups = (d_in + 511) / 512;
   int ks = 1;

@@ -80,7 +80,8 @@ void launch_fill_u32(void* p, size_t n_words, uint32_t v, hipStream_t st);
 void launch_set_slot_rank(int32_t* table, int id, int rank, hipStream_t st);
 
 // bf16 path for larger token counts (kernels_gemm.hip); the shrink alone
-// (k_shrink2, and k_vfinal when ks > 1) writes pos_info and v_fin
+// (k_shrink_short, or k_shrink2 and k_vfinal when ks > 1) writes pos_info
+// and v_fin
 void launch_linear_bf16(const LinearArgs& a, hipStream_t st);
 void launch_shrink_bf16(const LinearArgs& a, hipStream_t st);
 
