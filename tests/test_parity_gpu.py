@@ -324,3 +324,19 @@ def test_short_segment_shrink_with_token_index(capfd, monkeypatch):
     log(f"[parity] short segments with token_index: T={cu.n_tokens}, {len(ss) - 1} segments")
     y_ref = oracle.case_linear(cu, 1, threads=oracle_threads())
     compare(y_host(y), y_ref, BF16_TOL, "short segments with token_index")
+
+
+@pytest.mark.parametrize("shrink", ["short", "mfma"])
+def test_max_segments(shrink, monkeypatch):
+    # MLORA_MAX_SEGMENTS one-token segments (adapter ids cycling over 64
+    # adapters, so an adapter serves many segments) on a small layer: the
+    # shrinks' segment scans and LDS tables at their largest, T = 16384
+    if shrink == "mfma":
+        monkeypatch.setenv("MLORA_FORCE_SHRINK", "mfma")
+    S = 16384   # MLORA_MAX_SEGMENTS (include/mlora.h)
+    ids = [s % 64 for s in range(S)]
+    log(f"[parity] max segments ({shrink} shrink): 64->48, T={S}, {S} segments")
+    c = make_custom_case(140, "bf16", 64, 48, ids, {a: [4, 8, 16][a % 3] for a in range(64)})
+    assert len(c.seg_start) - 1 == S
+    dc = DeviceCase(c)
+    check_case(dc, 1, what=f"max segments {shrink} lora_on=1")
