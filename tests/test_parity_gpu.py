@@ -340,3 +340,21 @@ def test_max_segments(shrink, monkeypatch):
     assert len(c.seg_start) - 1 == S
     dc = DeviceCase(c)
     check_case(dc, 1, what=f"max segments {shrink} lora_on=1")
+
+
+MAX_DIM = 1 << 17   # MLORA_MAX_DIM (include/mlora.h)
+
+
+@pytest.mark.parametrize("d_in,d_out", [(MAX_DIM, 8), (64, MAX_DIM)])
+@pytest.mark.parametrize("T", [40, 100])
+def test_max_dims(d_in, d_out, T):
+    # the largest d_in (128 decode chunks of 1024; a 4096-step GEMM k loop)
+    # and the largest d_out (2048 decode tiles), on both paths
+    rng = np.random.default_rng(150 + T)
+    ids = sorted(rng.integers(-1, 4, size=T).tolist())
+    log(f"[parity] max dims: {d_in}->{d_out}, T={T}")
+    c = make_custom_case(150 + T, "bf16", d_in, d_out, ids, {0: 16, 1: 8, 2: 4, 3: 16})
+    dc = DeviceCase(c)
+    rows = sample_rows(c, 8) if d_out == MAX_DIM else None
+    check_case(dc, 1, rows, what=f"max dims {d_in}->{d_out} T={T} lora_on=1")
+    check_case(dc, 0, rows, what=f"max dims {d_in}->{d_out} T={T} lora_on=0")
