@@ -358,3 +358,18 @@ def test_max_dims(d_in, d_out, T):
     rows = sample_rows(c, 8) if d_out == MAX_DIM else None
     check_case(dc, 1, rows, what=f"max dims {d_in}->{d_out} T={T} lora_on=1")
     check_case(dc, 0, rows, what=f"max dims {d_in}->{d_out} T={T} lora_on=0")
+
+
+@pytest.mark.parametrize("sorted_input", [True, False])
+def test_max_rank_gemm_path(sorted_input):
+    # MLORA_MAX_RANK (256) and odd large ranks on the tiled-GEMM path: the
+    # epilogue's four 64-column rank chunks, the shrink's several passes
+    rng = np.random.default_rng(160)
+    ids = rng.integers(-1, 5, size=150)
+    ids = np.sort(ids) if sorted_input else ids
+    ranks = {0: 256, 1: 200, 2: 1, 3: 129, 4: 64}
+    log(f"[parity] max rank on the GEMM path: 264->130, T=150, sorted={sorted_input}")
+    c = make_custom_case(160, "bf16", 264, 130, ids.tolist(), ranks, sorted_input=sorted_input)
+    dc = DeviceCase(c)
+    check_case(dc, 1, what=f"max rank sorted={sorted_input} lora_on=1")
+    check_case(dc, 0, what=f"max rank sorted={sorted_input} lora_on=0")
