@@ -190,3 +190,25 @@ def test_fused_merge_equals_per_projection_merges():
         torch.cuda.synchronize()
         assert np.array_equal(Wm[n0:n0 + c.d_out], ref), c.name
         n0 += c.d_out
+
+
+@pytest.mark.parametrize("T", [40, 200])
+def test_fused_max_slices(T):
+    # MLORA_MAX_SLICES (8) stacked projections of 48 rows, equal ranks (the
+    # windowed expand), on the decode and the GEMM path; a ninth slice is refused
+    ids = sorted(np.random.default_rng(170 + T).integers(-1, 5, size=T).tolist())
+    slices = _custom_slices(720, 256, [48] * 8, [8] * 8, ids, 5)
+    log(f"[fused] 8 slices of 48 rows, rank 8 each, T={T}")
+    dc = FusedDeviceCase(slices)
+    for lora_on in (1, 0):
+        y = y_host(dc.run(lora_on))
+        y_ref = oracle.fused_case_linear(slices, lora_on, threads=oracle_threads())
+        worst = compare(y, y_ref, BF16_TOL, f"8 slices T={T} lora_on={lora_on}")
+        log(f"  lora_on={lora_on}: max err/bound {worst:.3f}")
+    ml = dc.ml
+    pool = ml.Pool(64, 9 * 8, torch.bfloat16, 9 * 4, 1)
+    A = torch.zeros(4, 64, dtype=torch.bfloat16, device="cuda")
+    B = torch.zeros(8, 4, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ml.MloraError) as e:
+        pool.register_fused(0, [(A, B)] * 9)
+    assert e.value.code == ml.STATUS_CODE["MLORA_ERR_SHAPE"]
