@@ -69,6 +69,8 @@ SHAPES = [
     (602, 4096, 1024, [3], {3: 16}),
     (603, 1040, 4100, sorted(np.random.default_rng(603).integers(0, 20, size=33).tolist()), {a: 16 for a in range(20)}),
     (604, 14336, 256, sorted(np.random.default_rng(604).integers(-1, 4, size=17).tolist()), {a: 64 for a in range(4)}),
+    # the largest d_in (MLORA_MAX_DIM): 256 chunks of 512 columns
+    (607, 1 << 17, 8, sorted(np.random.default_rng(607).integers(-1, 3, size=24).tolist()), {a: 16 for a in range(3)}),
 ]
 
 
