@@ -71,6 +71,8 @@ CASES = [
     ("bf16", 136, 70, 72, 1.5, True),          # two rank chunks
     ("bf16", 264, 33, 256, 0.5, False),        # the largest rank, four chunks
     ("bf16", 8, 1, 1, 3.0, False),             # smallest shape
+    ("bf16", 1 << 17, 8, 16, 2.0, True),       # the largest d_in (MLORA_MAX_DIM)
+    ("bf16", 64, 1 << 17, 64, -1.0, False),    # the largest d_out
     ("f32", 256, 256, 8, 2.0, False),          # the fp32 tiny shape
     ("f32", 100, 37, 5, -1.0, True),           # ragged fp32
 ]
