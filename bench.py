@@ -60,8 +60,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode_bf16",
-                    choices=["decode_bf16", "verify_bf16", "hetero_bf16", "prefill_bf16", "tiny_f32",
+    ap.add_argument("--workload", default="all",
+                    help="all (default): the decode batch as the headline plus every other "
+                         "configuration under 'configs'; or one workload",
+                    choices=["all", "decode_bf16", "verify_bf16", "hetero_bf16", "prefill_bf16", "tiny_f32",
                              "merge_bf16", "fused_qkv_decode", "fused_gateup_verify",
                              "fused_qkv_prefill", "fused_gateup_prefill", "cycle_verify", "decode_fp8w"])
     ap.add_argument("--proj", default="q", help="prefill projection (also the merge shape)")
@@ -131,7 +133,7 @@ def ingest_counters(workload: str, kernels, fetch_csv: str, write_csv: str) -> d
     return out
 
 
-def graph_timed(step, n_sets: int, steps: int, warmup: int) -> float:
+def graph_timed(step, n_sets: int, steps: int, warmup: int, offset: int = 0) -> float:
     """ms per step over exactly `steps` calls replayed from HIP graphs: one
     graph holds n_sets consecutive calls (one per buffer set), a second one
     the remainder. Launch costs on the host drop out; the GPU runs the
@@ -142,19 +144,21 @@ def graph_timed(step, n_sets: int, steps: int, warmup: int) -> float:
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
         for i in range(max(warmup, 1)):
-            step(i)
+            step(offset + i)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
+    # the replays go on from the set after the warm-up's last
+    o = offset + max(warmup, 1)
     full, tail = steps // n_sets, steps % n_sets
     g_full, g_tail = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
     if full:
         with torch.cuda.graph(g_full):
             for i in range(n_sets):
-                step(i)
+                step(o + i)
     if tail:
         with torch.cuda.graph(g_tail):
             for i in range(tail):
-                step(i)
+                step(o + i)
     if full:
         g_full.replay()
     torch.cuda.synchronize()
@@ -264,7 +268,7 @@ def bench_merge(args):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for i in range(steps):
+        for i in range(warmup, warmup + steps):   # on from the warm-up's last set
             Wi, Wo, pool = sets[i % n_sets]
             ml.merge_adapter(Wi, pool, 0, 2.0, out=Wo)
         e1.record(stream)
@@ -290,7 +294,7 @@ def bench_merge(args):
     c0 = torch.cuda.Event(enable_timing=True)
     c1 = torch.cuda.Event(enable_timing=True)
     c0.record(stream)
-    for i in range(args.steps):
+    for i in range(args.warmup, args.warmup + args.steps):
         sets[i % n_sets][1].copy_(sets[i % n_sets][0])
     c1.record(stream)
     c1.synchronize()
@@ -409,7 +413,7 @@ def bench_fused(args):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for i in range(args.steps):
+        for i in range(args.warmup, args.warmup + args.steps):   # on from the warm-up's last set
             fn(i)
         e1.record(stream)
         e1.synchronize()
@@ -496,7 +500,7 @@ def bench_cycle(args):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for i in range(args.steps):
+        for i in range(args.warmup, args.warmup + args.steps):   # on from the warm-up's last set
             step(i)
         e1.record(stream)
         e1.synchronize()
@@ -585,7 +589,7 @@ def bench_fp8w(args):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for i in range(steps):
+        for i in range(warmup, warmup + steps):   # on from the warm-up's last set
             step(i)
         e1.record(stream)
         e1.synchronize()
@@ -637,6 +641,223 @@ def bench_fp8w(args):
     print(json.dumps(out), flush=True)
 
 
+def cpu_threads() -> int:
+    """Host threads the oracle baseline runs on: every CPU in this process's
+    affinity mask."""
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:
+        return max(1, os.cpu_count() or 1)
+
+
+def case_work(case):
+    """Algorithmic bytes and flops of one layer call, LoRA-on and LoRA-off:
+    bytes = W + touched adapters' A and B + x + y; flops = 2 T d_in d_out +
+    sum over tokens of 2 r (d_in + d_out)."""
+    import numpy as np
+    T, d_in, d_out = case.n_tokens, case.d_in, case.d_out
+    es = 2 if case.dtype == "bf16" else 4
+    touched = case.touched_adapters()
+    lora_bytes = sum((case.adapters[a].rank * d_in + d_out * case.adapters[a].rank) * es for a in touched)
+    base_bytes = (d_out * d_in + T * d_in + T * d_out) * es
+    ranks = np.array([case.adapters[int(a)].rank if a >= 0 else 0 for a in case.token_adapter])
+    flops_off = 2.0 * T * d_in * d_out
+    flops_on = flops_off + float(np.sum(2.0 * ranks * (d_in + d_out)))
+    return base_bytes + lora_bytes, base_bytes, flops_on, flops_off
+
+
+def measure_layer(case, args, label: str):
+    """LoRA-on and LoRA-off time of one workload's layer call (ms per call).
+
+    Every call takes the next buffer set (W, adapter pool, x, y, workspace)
+    of a rotation covering >= args.rotate_gib GiB, counting on from the
+    warm-up calls, so no timed call reads a set touched fewer than
+    n_sets - 1 calls earlier: the bytes come from HBM, not from the 256 MB
+    Infinity Cache. Returns a dict of times and the set geometry."""
+    import numpy as np
+    import torch
+    import rank_adapter_gemm_segmented_amd as ml
+    from gpu_util import f32, i32, to_dev
+
+    dev = torch.device("cuda:0")
+    T, d_in, d_out = case.n_tokens, case.d_in, case.d_out
+    es = 2 if case.dtype == "bf16" else 4
+    tdt = torch.bfloat16 if case.dtype == "bf16" else torch.float32
+    W0 = to_dev(case.W, case.dtype)
+    x0 = to_dev(case.x, case.dtype)
+    pool0 = ml.Pool(d_in, d_out, tdt, case.max_rank, case.capacity)
+    for aid in sorted(case.adapters):
+        ad = case.adapters[aid]
+        pool0.register(aid, to_dev(ad.A, case.dtype), to_dev(ad.B, case.dtype))
+    set_bytes = W0.numel() * es + pool0.arena.numel() + x0.numel() * es + T * d_out * es
+    n_sets = 2 if args.profile else max(3, int(np.ceil(args.rotate_gib * (1 << 30) / set_bytes)))
+    sets = []
+    for i in range(n_sets):
+        if i == 0:
+            W, x, pool = W0, x0, pool0
+        else:
+            W, x = W0.clone(), x0.clone()
+            pool = ml.Pool(d_in, d_out, tdt, case.max_rank, case.capacity)
+            pool.arena.copy_(pool0.arena)
+        sets.append((W, x, pool, torch.empty((T, d_out), dtype=tdt, device=dev), pool.workspace(T)))
+    if case.sorted_input:
+        meta = (i32(case.seg_start), i32(case.seg_adapter), i32(case.seg_rank), f32(case.seg_scale))
+    else:
+        tok, sc = i32(case.token_adapter), f32(case.adapter_scale)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    rot = [0]   # rotation position: the next call's buffer set
+
+    def step(i, lora_on):
+        W, x, pool, y, ws = sets[i % n_sets]
+        if case.sorted_input:
+            ml.linear(x, W, pool, *meta, lora_on=lora_on, out=y, workspace=ws)
+        else:
+            ml.linear_tokens(x, W, pool, tok, sc, lora_on=lora_on, out=y, workspace=ws)
+
+    def timed(lora_on, steps, warmup):
+        for _ in range(warmup):
+            step(rot[0], lora_on)
+            rot[0] += 1
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            step(rot[0], lora_on)
+            rot[0] += 1
+        e1.record(stream)
+        e1.synchronize()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps   # ms per call
+
+    res = {"n_sets": n_sets, "set_bytes": set_bytes}
+    if args.profile:
+        # counter runs: LoRA-on calls only, then a copy of known size
+        timed(1, 5, 2)
+        print(f"[bench] {label}: 7 lora_on calls done", file=sys.stderr, flush=True)
+        n = 256 << 20
+        src = torch.ones(n // 2, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] calibration copy of {n} bytes done", file=sys.stderr, flush=True)
+        return res
+    res["ms_on_eager"] = timed(1, args.steps, args.warmup)
+    res["ms_off_eager"] = timed(0, args.steps, args.warmup)
+    res["ms_on"], res["ms_off"] = res["ms_on_eager"], res["ms_off_eager"]
+    if args.graph:
+        for key, lo in (("ms_on", 1), ("ms_off", 0)):
+            res[key] = graph_timed(lambda i, lo=lo: step(i, lo), n_sets, args.steps, args.warmup,
+                                   offset=rot[0])
+            rot[0] += args.warmup
+    print(f"[bench] {label}: lora_on {res['ms_on'] * 1e3:.2f} us/call, lora_off {res['ms_off'] * 1e3:.2f} "
+          f"us/call ({'graph replay' if args.graph else 'eager'}), {n_sets} buffer sets of "
+          f"{set_bytes / 2**20:.1f} MiB", file=sys.stderr, flush=True)
+    del sets, pool0, W0, x0
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def layer_summary(case, res, args) -> dict:
+    """Per-workload figures of a measure_layer result: times, rates, the
+    LoRA-on overhead beside its byte (or flop) floor ratio, and the roofline
+    of the LoRA-on call (HBM-bound shapes against 8 TB/s, the prefill
+    shapes against the 2.5 PFLOP/s bf16 MFMA peak)."""
+    bytes_on, bytes_off, flops_on, flops_off = case_work(case)
+    ms_on, ms_off = res["ms_on"], res["ms_off"]
+    gbs_on = bytes_on / (ms_on * 1e-3) / 1e9
+    gbs_off = bytes_off / (ms_off * 1e-3) / 1e9
+    tf_on = flops_on / (ms_on * 1e-3) / 1e12
+    tf_off = flops_off / (ms_off * 1e-3) / 1e12
+    mfma = case.name.startswith("prefill")
+    roof = {"bound": "hbm", "achieved": round(gbs_on, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs_on / HBM_PEAK_GBS, 4)}
+    roof_off = {"frac": round(gbs_off / HBM_PEAK_GBS, 4)}
+    if mfma:
+        roof = {"bound": "mfma", "achieved": round(tf_on, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tf_on / MFMA_BF16_PEAK_TFLOPS, 4)}
+        roof_off = {"frac": round(tf_off / MFMA_BF16_PEAK_TFLOPS, 4)}
+    if case.dtype == "f32":
+        roof["note"] = "bound by launch latency: its bytes take well under a microsecond at 8 TB/s"
+    roof.update({"traffic": counted_traffic(case.name), "algorithmic_bytes": bytes_on,
+                 "us_per_call": round(ms_on * 1e3, 3), "kernels": layer_kernels(case),
+                 "kernel_source_hash": kernel_source_hash()})
+    touched = case.touched_adapters()
+    return {
+        "tokens": case.n_tokens, "d_in": case.d_in, "d_out": case.d_out, "dtype": case.dtype,
+        "adapters_touched": len(touched), "segments": case.n_seg if case.sorted_input else None,
+        "sorted_input": bool(case.sorted_input),
+        "ranks": sorted(set(case.adapters[a].rank for a in touched)),
+        "us_lora_on": round(ms_on * 1e3, 3), "us_lora_off": round(ms_off * 1e3, 3),
+        "gbs_lora_on": round(gbs_on, 1), "gbs_lora_off": round(gbs_off, 1),
+        "tflops_lora_on": round(tf_on, 2), "tflops_lora_off": round(tf_off, 2),
+        "unique_bytes_lora_on": bytes_on, "unique_bytes_lora_off": bytes_off,
+        "lora_on_overhead": round(ms_on / ms_off - 1.0, 4),
+        "floor_ratio": round((flops_on / flops_off) if mfma else (bytes_on / bytes_off), 4),
+        "floor_ratio_of": "flops" if mfma else "bytes",
+        "lora_off_frac": roof_off["frac"],
+        "buffer_sets": res["n_sets"],
+        "roofline": roof,
+    }
+
+
+def cpu_baseline(case, args) -> dict:
+    """The fp64 oracle over a bounded sample of the workload's batch (the
+    whole batch when it is small), timed on every CPU of the affinity mask
+    and once on one thread; value scaled to the whole batch."""
+    import numpy as np
+    import oracle
+    threads = cpu_threads()
+    T, d_in, d_out = case.n_tokens, case.d_in, case.d_out
+    bytes_on, _, flops_on, _ = case_work(case)
+    pool_o = oracle.PackedPool(case.adapters, case.capacity, d_in, d_out)
+    rows, n_rows = None, T
+    max_rows = max(1, int(4e10 / (2.0 * d_in * d_out)))
+    if T > max_rows:
+        rows = np.arange(max_rows, dtype=np.int32)
+        n_rows = max_rows
+    reps, t_total = 0, 0.0
+    while t_total * threads < args.cpu_seconds or reps == 0:
+        t0 = time.perf_counter()
+        oracle.case_linear(case, 1, rows=rows, threads=threads, pool=pool_o)
+        t_total += time.perf_counter() - t0
+        reps += 1
+        if reps >= 50:
+            break
+    t_batch = t_total / reps * (T / n_rows)
+    # the same sample on one thread, once (outputs are bitwise the same at any thread count)
+    rows1 = rows if rows is not None else np.arange(min(T, max(1, n_rows // 4)), dtype=np.int32)
+    t0 = time.perf_counter()
+    oracle.case_linear(case, 1, rows=rows1, threads=1, pool=pool_o)
+    t_1 = (time.perf_counter() - t0) * (T / len(rows1))
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "")
+    except OSError:
+        pass
+    return {"value": round(bytes_on / t_batch / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{n_rows} of {T} rows of the {case.name} batch, lora_on=1, fp64, "
+                      f"{reps} repetitions, {t_total:.1f} s wall on all {threads} CPUs of the affinity "
+                      f"mask; value scaled to the whole batch",
+            "seconds_per_batch": round(t_batch, 4),
+            "single_thread": {"seconds_per_batch": round(t_1, 4),
+                              "value": round(bytes_on / t_1 / 1e9, 4),
+                              "sample": f"{len(rows1)} rows, once, scaled to the whole batch"},
+            "gflops_fp64": round(flops_on / t_batch / 1e9, 2),
+            "cpu_model": cpu_model}
+
+
+# The configurations the default run measures besides the headline (decode):
+# the fp32 tiny case, the verify pass, the heterogeneous-rank batch and the
+# seven projections of one decoder layer at the prefill batch.
+OTHER_CONFIGS = [("tiny_f32", "q"), ("verify_bf16", "q"), ("hetero_bf16", "q")] + [
+    ("prefill_bf16", p) for p in ("q", "k", "v", "o", "gate", "up", "down")]
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -657,191 +878,57 @@ def main():
         bench_fp8w(args)
         return
 
-    import numpy as np
     import torch
     sys.path.insert(0, os.path.join(ROOT, "tests"))
-    import rank_adapter_gemm_segmented_amd as ml
-    from gpu_util import f32, i32, to_dev
     from mlora_inputs import make_case
 
-    case = make_case(args.workload, args.proj)
+    head = "decode_bf16" if args.workload == "all" else args.workload
+    case = make_case(head, args.proj)
     if args.ingest_counters:
         ent = ingest_counters(case.name, layer_kernels(case), *args.ingest_counters)
         print(json.dumps({case.name: ent}))
         return
     torch.cuda.set_device(0)
-    dev = torch.device("cuda:0")
-    T, d_in, d_out = case.n_tokens, case.d_in, case.d_out
-    es = 2 if case.dtype == "bf16" else 4
-    touched = case.touched_adapters()
-    lora_bytes = sum((case.adapters[a].rank * d_in + d_out * case.adapters[a].rank) * es for a in touched)
-    base_bytes = (d_out * d_in + T * d_in + T * d_out) * es
-    bytes_on, bytes_off = base_bytes + lora_bytes, base_bytes
-    ranks = np.array([case.adapters[int(a)].rank if a >= 0 else 0 for a in case.token_adapter])
-    flops_off = 2.0 * T * d_in * d_out
-    flops_on = flops_off + float(np.sum(2.0 * ranks * (d_in + d_out)))
-
-    # ---- buffer sets -------------------------------------------------------
-    tdt = torch.bfloat16 if case.dtype == "bf16" else torch.float32
-    W0 = to_dev(case.W, case.dtype)
-    x0 = to_dev(case.x, case.dtype)
-    pool0 = ml.Pool(d_in, d_out, tdt, case.max_rank, case.capacity)
-    for aid in sorted(case.adapters):
-        ad = case.adapters[aid]
-        pool0.register(aid, to_dev(ad.A, case.dtype), to_dev(ad.B, case.dtype))
-    set_bytes = W0.numel() * es + pool0.arena.numel() + x0.numel() * es + T * d_out * es
-    n_sets = 2 if args.profile else max(2, int(np.ceil(args.rotate_gib * (1 << 30) / set_bytes)))
-    sets = []
-    for i in range(n_sets):
-        if i == 0:
-            W, x, pool = W0, x0, pool0
-        else:
-            W, x = W0.clone(), x0.clone()
-            pool = ml.Pool(d_in, d_out, tdt, case.max_rank, case.capacity)
-            pool.arena.copy_(pool0.arena)
-        y = torch.empty((T, d_out), dtype=tdt, device=dev)
-        ws = pool.workspace(T)
-        sets.append((W, x, pool, y, ws))
-    if case.sorted_input:
-        meta = (i32(case.seg_start), i32(case.seg_adapter), i32(case.seg_rank), f32(case.seg_scale))
-    else:
-        tok = i32(case.token_adapter)
-        sc = f32(case.adapter_scale)
-    torch.cuda.synchronize()
-
-    stream = torch.cuda.current_stream()
-
-    def step(i, lora_on):
-        W, x, pool, y, ws = sets[i % n_sets]
-        if case.sorted_input:
-            ml.linear(x, W, pool, *meta, lora_on=lora_on, out=y, workspace=ws)
-        else:
-            ml.linear_tokens(x, W, pool, tok, sc, lora_on=lora_on, out=y, workspace=ws)
-
-    def timed(lora_on, steps, warmup):
-        for i in range(warmup):
-            step(i, lora_on)
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(steps):
-            step(i, lora_on)
-        e1.record(stream)
-        e1.synchronize()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / steps   # ms per step
-
+    res = measure_layer(case, args, case.name)
     if args.profile:
-        # counter runs: LoRA-on calls only, then a copy of known size
-        timed(1, 5, 2)
-        print(f"[bench] {case.name}: 7 lora_on calls done", file=sys.stderr, flush=True)
-        # calibration copy of a known size for the FETCH_SIZE / WRITE_SIZE counters
-        n = 256 << 20
-        src = torch.ones(n // 2, dtype=torch.bfloat16, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        print(f"[bench] calibration copy of {n} bytes done", file=sys.stderr, flush=True)
         return
+    summ = layer_summary(case, res, args)
+    others = {}
+    if args.workload == "all":
+        for name, proj in OTHER_CONFIGS:
+            c = make_case(name, proj)
+            others[c.name] = layer_summary(c, measure_layer(c, args, c.name), args)
+            del c
+    cpu = None if args.no_cpu_baseline else cpu_baseline(case, args)
 
-    ms_on_eager = timed(1, args.steps, args.warmup)
-    ms_off_eager = timed(0, args.steps, args.warmup)
-    ms_on, ms_off = ms_on_eager, ms_off_eager
-    if args.graph:
-        ms_on = graph_timed(lambda i: step(i, 1), n_sets, args.steps, args.warmup)
-        ms_off = graph_timed(lambda i: step(i, 0), n_sets, args.steps, args.warmup)
-    print(f"[bench] {case.name}: lora_on {ms_on * 1e3:.2f} us/step, lora_off {ms_off * 1e3:.2f} us/step "
-          f"({'graph replay' if args.graph else 'eager'}; eager {ms_on_eager * 1e3:.2f} / {ms_off_eager * 1e3:.2f}), "
-          f"{n_sets} buffer sets of {set_bytes / 2**20:.1f} MiB", file=sys.stderr, flush=True)
-
-    gbs_on = bytes_on / (ms_on * 1e-3) / 1e9
-    gbs_off = bytes_off / (ms_off * 1e-3) / 1e9
-    tf_on = flops_on / (ms_on * 1e-3) / 1e12
-    tf_off = flops_off / (ms_off * 1e-3) / 1e12
-
-    # ---- HBM traffic from committed counter runs (only if sources match) ----
-    traffic = counted_traffic(case.name)
-    src_hash = kernel_source_hash()
-
-    kernels = layer_kernels(case)
-    roofline = {"bound": "hbm", "achieved": round(gbs_on, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gbs_on / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "algorithmic_bytes": bytes_on, "us_per_call": round(ms_on * 1e3, 3),
-                "kernels": kernels, "kernel_source_hash": src_hash}
-    if case.name.startswith("prefill"):
-        roofline.update({"bound": "mfma", "achieved": round(tf_on, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tf_on / MFMA_BF16_PEAK_TFLOPS, 4)})
-
-    # ---- CPU baseline: the fp64 oracle on the host cores -------------------
-    cpu = None
-    if not args.no_cpu_baseline:
-        import oracle
-        threads = len(os.sched_getaffinity(0))
-        if os.environ.get("OMP_NUM_THREADS", "").isdigit():
-            threads = min(threads, int(os.environ["OMP_NUM_THREADS"]))
-        threads = max(1, min(threads, 16))
-        pool_o = oracle.PackedPool(case.adapters, case.capacity, d_in, d_out)
-        rows = None
-        n_rows = T
-        # bounded sample: whole batch when it is small, else a prefix of rows
-        per_row = 2.0 * d_in * d_out
-        max_rows = max(1, int(4e10 / per_row))
-        if T > max_rows:
-            rows = np.arange(max_rows, dtype=np.int32)
-            n_rows = max_rows
-        reps, t_total = 0, 0.0
-        while t_total * threads < args.cpu_seconds or reps == 0:
-            t0 = time.perf_counter()
-            oracle.case_linear(case, 1, rows=rows, threads=threads, pool=pool_o)
-            t_total += time.perf_counter() - t0
-            reps += 1
-            if reps >= 50:
-                break
-        t_batch = t_total / reps * (T / n_rows)
-        # the same sample on one thread, once (outputs are bitwise the same at any thread count)
-        rows1 = rows if rows is not None else np.arange(min(T, max(1, n_rows // 4)), dtype=np.int32)
-        t0 = time.perf_counter()
-        oracle.case_linear(case, 1, rows=rows1, threads=1, pool=pool_o)
-        t_1 = (time.perf_counter() - t0) * (T / len(rows1))
-        cpu_model = ""
-        try:
-            with open("/proc/cpuinfo") as fh:
-                cpu_model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "")
-        except OSError:
-            pass
-        cpu = {"value": round(bytes_on / t_batch / 1e9, 4), "unit": "GB/s", "cores": threads,
-               "kind": "oracle",
-               "sample": f"{n_rows} of {T} rows of the {case.name} batch, lora_on=1, fp64, "
-                         f"{reps} repetitions, {t_total:.1f} s wall; value scaled to the whole batch",
-               "seconds_per_batch": round(t_batch, 4),
-               "single_thread": {"seconds_per_batch": round(t_1, 4),
-                                 "value": round(bytes_on / t_1 / 1e9, 4),
-                                 "sample": f"{len(rows1)} rows, once, scaled to the whole batch"},
-               "gflops_fp64": round(flops_on / t_batch / 1e9, 2),
-               "cpu_model": cpu_model}
-
-    cfg = {"workload": case.name, "tokens": T, "d_in": d_in, "d_out": d_out,
-           "adapters_touched": len(touched), "segments": case.n_seg if case.sorted_input else None,
-           "ranks": sorted(set(case.adapters[a].rank for a in touched)), "lora_on": 1,
-           "buffer_sets": n_sets, "unique_bytes_lora_on": bytes_on, "unique_bytes_lora_off": bytes_off}
+    bytes_on, bytes_off = summ["unique_bytes_lora_on"], summ["unique_bytes_lora_off"]
+    cfg = {"workload": case.name, "tokens": case.n_tokens, "d_in": case.d_in, "d_out": case.d_out,
+           "adapters_touched": summ["adapters_touched"], "segments": summ["segments"],
+           "ranks": summ["ranks"], "lora_on": 1, "buffer_sets": res["n_sets"],
+           "unique_bytes_lora_on": bytes_on, "unique_bytes_lora_off": bytes_off}
+    ms_on, ms_off = res["ms_on"], res["ms_off"]
     out = {
-        "metric": METRIC, "value": round(gbs_on, 1), "unit": "GB/s", "n_gpus": 1,
+        "metric": METRIC, "value": summ["gbs_lora_on"], "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_on, 6),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": case.dtype,
         "data": "synthetic (seeded Gaussian weights, adapters and activations)",
         "config": cfg,
-        "tflops": round(tf_on, 2), "pct_hbm_roofline": round(100 * gbs_on / HBM_PEAK_GBS, 2),
-        "lora_off": {"ms_per_step": round(ms_off, 6), "gbs": round(gbs_off, 1), "tflops": round(tf_off, 2),
-                     "pct_hbm_roofline": round(100 * gbs_off / HBM_PEAK_GBS, 2)},
-        "lora_on_overhead": round(ms_on / ms_off - 1.0, 4),
+        "tflops": summ["tflops_lora_on"], "pct_hbm_roofline": round(100 * summ["gbs_lora_on"] / HBM_PEAK_GBS, 2),
+        "lora_off": {"ms_per_step": round(ms_off, 6), "gbs": summ["gbs_lora_off"],
+                     "tflops": summ["tflops_lora_off"],
+                     "pct_hbm_roofline": round(100 * summ["gbs_lora_off"] / HBM_PEAK_GBS, 2)},
+        "lora_on_overhead": summ["lora_on_overhead"],
         "byte_floor_ratio": round(bytes_on / bytes_off, 4),
         "timing": ("K calls replayed from HIP graphs (one graph per pass over the buffer sets)"
-                   if args.graph else "K eager calls through the Python binding"),
-        "eager": {"ms_per_step_lora_on": round(ms_on_eager, 6), "ms_per_step_lora_off": round(ms_off_eager, 6)},
-        "roofline": roofline,
+                   if args.graph else "K eager calls through the Python binding, buffer sets rotated "
+                   "continuously from the warm-up on"),
+        "eager": {"ms_per_step_lora_on": round(res["ms_on_eager"], 6),
+                  "ms_per_step_lora_off": round(res["ms_off_eager"], 6)},
+        "roofline": summ["roofline"],
         "cpu_baseline": cpu,
     }
+    if others:
+        out["configs"] = others
     print(json.dumps(out), flush=True)
 
 

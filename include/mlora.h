@@ -9,9 +9,9 @@
  * which is the LoRA forward of "Multi-LoRA Serving in Practice", section "Core
  * Principle" (displayed formula), applied per request with one shared base
  * weight W and a per-request adapter (same section: the request names the
- * adapter it uses). The batch is partitioned into segments, one adapter per
- * segment ("InvisibleLoRA" abstract: requests are partitioned across active
- * adapters; "Multi-LoRA Serving in Practice", section "4. Batching":
+ * adapter it uses). The batch is split into segments, one adapter per
+ * segment (the "InvisibleLoRA" abstract divides a batch's requests among the
+ * adapters in use; "Multi-LoRA Serving in Practice", section "4. Batching":
  * adapter-aware batching groups requests of one adapter). lora_on = 0 is the
  * InvisibleLoRA LoRA-off drafter pass (base model alone); lora_on = 1 is its
  * LoRA-on verification pass.

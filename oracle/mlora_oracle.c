@@ -14,8 +14,8 @@
  * "Core Principle" (its displayed formula: the base product plus a scaled
  * low-rank product, with A applied first and B second). The adapter a and its
  * scale come from the token's segment: the batch is partitioned into segments,
- * one adapter each ("InvisibleLoRA" abstract: requests are partitioned across
- * active adapters). lora_on = 0 is that abstract's LoRA-off drafter pass,
+ * one adapter each (the "InvisibleLoRA" abstract splits a batch's requests
+ * among the adapters in use). lora_on = 0 is that abstract's LoRA-off drafter pass,
  * which runs the shared base model alone.
  *
  * Layouts (row-major): x [T, d_in], W [d_out, d_in], A_a [r_a, d_in],

@@ -62,6 +62,22 @@ __device__ __forceinline__ f32x16_t mfma32g(u32x4_t a, u32x4_t b, f32x16_t c) {
 constexpr int kShrMaxSeg = MLORA_MAX_SEGMENTS;  // segments the item scan handles
 constexpr int kShrLdsSeg = 4096;                // up to this many, adapters and ranks go to LDS too
 
+// Whether the shrinks keep the segments' adapters and ranks in LDS next to
+// the starts. Decided from the host's segment bound (sv.n_seg), never from a
+// device count, so the kernels' LDS layout and the host's allocation
+// (shrink_lds_bytes) always agree.
+__host__ __device__ __forceinline__ bool shrink_meta_in_lds(int n_seg_bound) {
+  return (n_seg_bound < kShrMaxSeg ? n_seg_bound : kShrMaxSeg) <= kShrLdsSeg;
+}
+
+// Dynamic LDS of a shrink launch: starts [S + 1] and, by the rule above,
+// adapters [S] and ranks [S], for S = the host's bound. The device count,
+// when there is one, never exceeds it.
+static size_t shrink_lds_bytes(int n_seg_bound) {
+  const int nseg = n_seg_bound < kShrMaxSeg ? n_seg_bound : kShrMaxSeg;
+  return (size_t)(shrink_meta_in_lds(n_seg_bound) ? 3 * nseg + 1 : nseg + 1) * sizeof(int);
+}
+
 template <int NRB, int NCB>
 __global__ __launch_bounds__(256) void k_shrink2(LinearArgs a) {
   constexpr int NQ = NRB * NCB * 4;     // accumulator floats per lane
@@ -71,9 +87,13 @@ __global__ __launch_bounds__(256) void k_shrink2(LinearArgs a) {
   const int T = a.T, d_in = a.d_in;
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid % kWave;
-  // segment starts [S + 1], and (S <= kShrLdsSeg) the adapters [S] and ranks [S]
+  // segment starts [S + 1], and the adapters [S] and ranks [S] when the
+  // host's segment bound is at most kShrLdsSeg. The choice follows the host
+  // bound, the count the host sized the dynamic LDS from (shrink_lds_bytes):
+  // with device-built segments S is read on the device and may be smaller
+  // than the bound, and a layout chosen from S could outgrow the allocation.
   extern __shared__ int sdyn[];
-  const bool meta_lds = S <= kShrLdsSeg;
+  const bool meta_lds = shrink_meta_in_lds(sv.n_seg);
   int* sst = sdyn;
   int* sad = sdyn + S + 1;
   int* srk = sdyn + 2 * S + 1;
@@ -326,7 +346,7 @@ __global__ __launch_bounds__(256) void k_shrink_short(LinearArgs a) {
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid % kWave;
   extern __shared__ int sdyn[];
-  const bool meta_lds = S <= kShrLdsSeg;
+  const bool meta_lds = shrink_meta_in_lds(sv.n_seg);   // same rule as k_shrink2
   int* sst = sdyn;
   int* sad = sdyn + S + 1;
   int* srk = sdyn + 2 * S + 1;
@@ -1052,7 +1072,7 @@ void launch_shrink_bf16(const LinearArgs& a, hipStream_t st) {
     const int rmax = a.pv.max_rank < 64 ? a.pv.max_rank : 64;
     const bool long_segs = a.T > 16 * a.seg_grid;
     const dim3 grid(shrink_items_bound(a.T, a.seg_grid), a.ks);
-    const size_t lds = (size_t)(nseg <= kShrLdsSeg ? 3 * nseg + 1 : nseg + 1) * sizeof(int);
+    const size_t lds = shrink_lds_bytes(a.seg_grid);
     if (shrink_short(a)) {
       // at most two positions per segment on average, one d_in chunk, ranks <= 16
       const dim3 gs((a.pv.max_rank + kSsRows - 1) / kSsRows, nseg + (a.T + kSsPos - 1) / kSsPos);

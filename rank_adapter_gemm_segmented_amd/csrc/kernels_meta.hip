@@ -1,7 +1,7 @@
 // kernels_meta.hip -- segment metadata kernels for gfx950.
 //
-// The batch is partitioned into segments, one adapter each ("InvisibleLoRA"
-// abstract: requests are partitioned across active adapters). Requests of the
+// The batch is split into segments, one adapter each (the "InvisibleLoRA"
+// abstract divides a batch's requests among the adapters in use). Requests of the
 // same adapter are grouped before the low-rank work ("Multi-LoRA Serving in
 // Practice", section "4. Batching", adapter-aware batching). These kernels
 // (a) map sorted positions to segments and adapters, (b) group an unsorted

@@ -1,11 +1,11 @@
 """Layer-level cost model of the InvisibleLoRA decoding cycle and its run-time gate.
 
-The *InvisibleLoRA* abstract describes the cycle: one LoRA-off pass of the shared
-base model proposes the next token of every request in the batch, and one
-LoRA-on pass verifies all proposals, so adapter work runs once per cycle
-instead of once per token. It adds a run-time gate that skips drafting on
-steps where the adapter cost cannot repay a draft pass, and reports median
-draft acceptance of 92-97%.
+Per the *InvisibleLoRA* abstract, the shared base model with every adapter
+switched off drafts one token for each request, and a single pass with the
+adapters switched on then checks all of those drafts together; the adapters
+thus run once per cycle, not once per generated token. A gate decides at run
+time whether a step drafts at all (drafting is dropped where it would not pay
+for itself), and the abstract quotes median acceptance rates of 92-97%.
 
 The abstract gives no formula for either. This module takes the plainest
 reading that the rest supports:
@@ -26,6 +26,8 @@ cache and sampling are outside the model.
 from __future__ import annotations
 
 from dataclasses import dataclass
+
+import numpy as np
 
 
 @dataclass(frozen=True)
@@ -50,3 +52,39 @@ def cycle_estimate(t_on_b: float, t_off_b: float, t_on_2b: float, alpha: float) 
 def break_even_alpha(t_on_b: float, t_off_b: float, t_on_2b: float) -> float:
     """Smallest acceptance rate at which drafting pays (may exceed 1: never)."""
     return (t_off_b + t_on_2b) / t_on_b - 1.0
+
+
+def verify_segments(draft_seg_start, tokens_per_request: int = 2) -> np.ndarray:
+    """Segment starts of the verification pass, from those of the draft pass.
+
+    The draft pass holds one position per request, with requests grouped by
+    adapter; the verification pass holds ``tokens_per_request`` consecutive
+    positions per request (its last committed token, then its draft) in the
+    same request order, so every segment keeps its adapter, rank and scale
+    and its bounds scale by ``tokens_per_request``."""
+    ss = np.asarray(draft_seg_start, dtype=np.int64)
+    if tokens_per_request < 1:
+        raise ValueError("a request holds at least one position")
+    if ss.ndim != 1 or ss.size < 1 or ss[0] != 0 or np.any(np.diff(ss) < 0):
+        raise ValueError("seg_start must start at 0 and be non-decreasing")
+    return (ss * tokens_per_request).astype(np.int32)
+
+
+def cycle_passes(linear, x_draft, x_verify, W, pool, seg_start, seg_adapter, seg_rank, seg_scale,
+                 tokens_per_request: int = 2, workspace=None):
+    """One decoding cycle of a layer through ``linear`` (the binding's
+    ``mlora_linear``): the LoRA-off draft pass over ``x_draft`` (one row per
+    request) and the LoRA-on verification pass over ``x_verify``
+    (``tokens_per_request`` rows per request, request-major). ``seg_*`` are
+    the draft pass's device metadata; the verification pass's starts come
+    from ``verify_segments``. Returns (y_draft, y_verify)."""
+    import torch
+    b = int(x_draft.shape[0])
+    if int(x_verify.shape[0]) != tokens_per_request * b:
+        raise ValueError("the verification batch holds tokens_per_request rows per request")
+    vss = torch.from_numpy(verify_segments(seg_start.cpu().numpy(), tokens_per_request)).to(seg_start.device)
+    y_draft = linear(x_draft, W, pool, seg_start, seg_adapter, seg_rank, seg_scale, lora_on=0,
+                     workspace=workspace)
+    y_verify = linear(x_verify, W, pool, vss, seg_adapter, seg_rank, seg_scale, lora_on=1,
+                      workspace=workspace)
+    return y_draft, y_verify

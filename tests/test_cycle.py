@@ -8,7 +8,9 @@ token is below a plain LoRA-on step's.
 """
 import pytest
 
-from rank_adapter_gemm_segmented_amd.cycle import break_even_alpha, cycle_estimate
+import numpy as np
+
+from rank_adapter_gemm_segmented_amd.cycle import break_even_alpha, cycle_estimate, verify_segments
 
 
 def test_break_even_is_the_gate_boundary():
@@ -41,3 +43,21 @@ def test_never_drafts_when_a_cycle_costs_two_steps_or_more():
     assert not cycle_estimate(10.0, 10.0, 10.0, 1.0).draft
     with pytest.raises(ValueError):
         cycle_estimate(10.0, 10.0, 10.0, 1.5)
+
+
+def test_verify_segments_keep_each_request_in_its_segment():
+    # draft: 5 requests, adapters grouped as [0, 0 | 3 | 7, 7]; verify: two
+    # positions per request, request-major, so every position 2q, 2q + 1
+    # falls in request q's segment
+    ss = np.array([0, 2, 3, 5], np.int32)
+    vs = verify_segments(ss)
+    assert vs.tolist() == [0, 4, 6, 10] and vs.dtype == np.int32
+    seg_of = lambda starts, p: int(np.searchsorted(starts, p, side="right") - 1)
+    for q in range(5):
+        for j in range(2):
+            assert seg_of(vs, 2 * q + j) == seg_of(ss, q)
+    assert verify_segments(ss, 3).tolist() == [0, 6, 9, 15]
+    with pytest.raises(ValueError):
+        verify_segments(np.array([1, 2], np.int32))
+    with pytest.raises(ValueError):
+        verify_segments(ss, 0)

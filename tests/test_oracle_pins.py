@@ -11,7 +11,7 @@ Sources of the facts pinned:
   (displayed formula, base product plus scale times B applied to A x).
 * Merged weights W = W0 + dW: "LoRA Inference" glossary, first paragraph
   (pinned for the layer and for the oracle's merge of one adapter).
-* LoRA-off pass = base model alone; batch partitioned across adapters:
+* LoRA-off pass = base model alone; batch split among the adapters in use:
   "InvisibleLoRA" abstract.
 * Grouping same-adapter requests: "Multi-LoRA Serving in Practice",
   section "4. Batching", the adapter-aware batching row of its table.
