@@ -82,8 +82,11 @@ WsLayout ws_layout(const mlora_pool_s* p, int T) {
   L.counts = take(t1 * 4);
   int n_tiles = 0, kc = 0, n_chunks = 0;
   decode_plan(p->d_in, p->d_out, &n_tiles, &kc, &n_chunks);
-  // shrink partial slices: split-K of the large-T path, or 8 waves per d_in chunk at T <= 64
-  const int splits = n_chunks * 8 > kMaxShrinkSplit ? n_chunks * 8 : kMaxShrinkSplit;
+  // shrink partial slices: split-K of the large-T path (at most
+  // kMaxShrinkSplit), and at T <= 64 also 8 waves per d_in chunk of the
+  // decode stream
+  const int dec_splits = n_chunks * 8;
+  const int splits = T <= 64 && dec_splits > kMaxShrinkSplit ? dec_splits : kMaxShrinkSplit;
   L.v_part = take((size_t)splits * T * r_ws_of(p->max_rank) * 4);
   // decode partial tiles, only for token counts the decode path takes
   const size_t tt = T <= 16 ? 16 : T <= 32 ? 32 : 64;
