@@ -192,6 +192,25 @@ int mlora_linear(const void* x, const void* W, mlora_pool_t pool, const int32_t*
                  const int32_t* token_index, int n_tokens, int n_seg, int lora_on, void* y,
                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* mlora_linear without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. The call allocates nothing (no hipMalloc,
+ * no hipFree, no allocating library routine); the layer's workspace is a
+ * library-owned device array of MLORA_NOALLOC_SCRATCH_BYTES bytes, one per
+ * GPU the library runs on, held until the process ends. Arguments, results
+ * and errors as mlora_linear (same kernels, same bits). A call whose
+ * workspace (mlora_workspace_bytes of its n_tokens) exceeds the scratch
+ * returns MLORA_ERR_WORKSPACE and launches nothing. Every call on one GPU
+ * shares that GPU's scratch, which keeps the last call's contents: calls on
+ * one GPU must not overlap (one stream, or ordered by events), or they race.
+ * The first call on a device looks up the scratch's device address
+ * (hipGetSymbolAddress) with that device current. */
+#define MLORA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int mlora_linear_noalloc(const void* x, const void* W, mlora_pool_t pool, const int32_t* seg_start,
+                         const int32_t* seg_adapter, const int32_t* seg_rank, const float* seg_scale,
+                         const int32_t* token_index, int n_tokens, int n_seg, int lora_on, void* y,
+                         hipStream_t stream);
+
 /* The layer with the base weight stored as FP8 and the adapters in bf16:
  *
  *     y_i = diag(w_scale) (Q x_i) + scale_s * B_a (A_a x_i),

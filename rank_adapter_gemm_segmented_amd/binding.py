@@ -58,6 +58,7 @@ def _load() -> ctypes.CDLL:
         "mlora_merge_adapter": ([P, P, P, I, ctypes.c_float, P], I),
         "mlora_register_adapter_fused": ([P, I, I, P, P, P, P, P], I),
         "mlora_linear_fp8w": ([P, P, P, P, P, P, P, P, P, I, I, I, P, P, SZ, P], I),
+        "mlora_linear_noalloc": ([P, P, P, P, P, P, P, P, I, I, I, P, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -209,6 +210,24 @@ def linear(x, W, pool: Pool, seg_start=None, seg_adapter=None, seg_rank=None, se
                              _ptr(seg_scale), _ptr(_i32(token_index, "token_index")), T, n_seg,
                              int(lora_on), _ptr(y), _ptr(ws), ws.numel(), _stream()),
            "mlora_linear")
+    return y
+
+
+def linear_noalloc(x, W, pool: Pool, seg_start=None, seg_adapter=None, seg_rank=None, seg_scale=None,
+                   lora_on: int = 1, token_index=None, out=None):
+    """``mlora_linear_noalloc``: ``linear`` with the library's own device
+    scratch as the workspace (the call allocates nothing; ``out`` should be
+    given by callers that cannot allocate either)."""
+    _check_xw(x, W, pool)
+    T = int(x.shape[0])
+    y = out if out is not None else torch.empty((T, pool.d_out), dtype=pool.dtype, device=x.device)
+    n_seg = int(seg_adapter.numel()) if seg_adapter is not None else 0
+    if seg_scale is not None and (seg_scale.dtype != torch.float32 or not seg_scale.is_contiguous()):
+        raise TypeError("seg_scale must be contiguous float32")
+    _check(_lib.mlora_linear_noalloc(_ptr(x), _ptr(W), pool.handle, _ptr(_i32(seg_start, "seg_start")),
+                                     _ptr(_i32(seg_adapter, "seg_adapter")), _ptr(_i32(seg_rank, "seg_rank")),
+                                     _ptr(seg_scale), _ptr(_i32(token_index, "token_index")), T, n_seg,
+                                     int(lora_on), _ptr(y), _stream()), "mlora_linear_noalloc")
     return y
 
 

@@ -1,10 +1,12 @@
 // api.hip -- the exported C ABI (include/mlora.h): adapter pool, workspace,
-// host-side validation and kernel dispatch. Host code only.
+// host-side validation and kernel dispatch, plus the device scratch array of
+// the entry point that allocates nothing.
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -217,6 +219,35 @@ int run_linear(const void* x, const void* W, mlora_pool_s* pool, const SegView& 
     launch_linear_f32(a, stream);
   }
   return check_launch();
+}
+
+// ---- scratch of the entry point that allocates nothing ----------------------
+// mlora_linear_noalloc runs the layer with its workspace in this file-scope
+// device array instead of a caller's buffer. Every GPU the library runs on
+// holds its own copy, at its own address, until the process ends. In host
+// code the array's name is only a stand-in: kernels and copies get the
+// device address from hipGetSymbolAddress, taken once per device (with that
+// device current) and kept in scratch_dev.
+static __device__ __align__(256) unsigned char scratch[MLORA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_dev[kMaxDevices] = {};
+
+// Device address of the current device's scratch (taken on the first call on
+// that device).
+int scratch_ptr(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MLORA_ERR_HIP;
+  if (dev >= kMaxDevices) return MLORA_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MLORA_ERR_HIP;
+    scratch_dev[dev] = p;
+  }
+  *out = scratch_dev[dev];
+  return MLORA_OK;
 }
 
 }  // namespace
@@ -434,6 +465,23 @@ int mlora_linear(const void* x, const void* W, mlora_pool_t pool, const int32_t*
     }
   }
   return run_linear(x, W, pool, sv, n_tokens, lora_on, y, (char*)workspace, stream);
+}
+
+int mlora_linear_noalloc(const void* x, const void* W, mlora_pool_t pool, const int32_t* seg_start,
+                         const int32_t* seg_adapter, const int32_t* seg_rank, const float* seg_scale,
+                         const int32_t* token_index, int n_tokens, int n_seg, int lora_on, void* y,
+                         hipStream_t stream) {
+  if (!pool) return MLORA_ERR_INVALID_ARG;
+  if (n_tokens < 0 || n_tokens > MLORA_MAX_TOKENS) return MLORA_ERR_SHAPE;
+  if (n_tokens == 0) return MLORA_OK;
+  // the whole workspace of the call must fit the scratch: larger calls are
+  // refused before anything runs
+  if (ws_layout(pool, n_tokens).total > (size_t)MLORA_NOALLOC_SCRATCH_BYTES) return MLORA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const int st = scratch_ptr(&ws);
+  if (st != MLORA_OK) return st;
+  return mlora_linear(x, W, pool, seg_start, seg_adapter, seg_rank, seg_scale, token_index, n_tokens,
+                      n_seg, lora_on, y, ws, (size_t)MLORA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int mlora_linear_fp8w(const void* x, const uint8_t* W_fp8, const float* w_scale, mlora_pool_t pool,
