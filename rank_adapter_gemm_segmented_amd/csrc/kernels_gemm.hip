@@ -569,29 +569,38 @@ __device__ __forceinline__ void vm_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-// KB: k per stage (32 or 64). A stage holds the tile's BR W rows then its BT
-// positions. DMA: the stages reach LDS by direct loads, in a ring of NB LDS
-// slots (NB - 1 in flight while one is multiplied); rows are 2 KB bytes,
-// unpadded, and 16-byte chunk c of row r sits in slot c ^ swz(r) of the row,
-// so the rows read together by one fragment load fall in distinct LDS banks.
-// Otherwise the stages pass through registers (NB - 1 in flight there) into
-// two LDS slots whose rows are padded to 2 KB + 16 bytes instead.
-template <int BR, int BT, int WR, int WT, int NB, int KB, bool DMA>
+// KB: k per stage (32 or 64). A stage is the tile's BR W rows and its BT
+// positions over KB columns. The stages reach LDS by direct loads into two
+// rings, one for the W rows (NB slots, NB - 1 stages in flight while one is
+// multiplied) and one for the positions (NX slots, NX - 1 in flight). Rows
+// are 2 KB bytes, unpadded, and 16-byte chunk c of row r sits in slot
+// c ^ swz(r) of the row, so the rows read together by one fragment load fall
+// in distinct LDS banks.
+template <int BR, int BT, int WR, int WT, int NB, int KB, int NX>
 struct GCfg {
   static constexpr int NWR = BR / WR, NWT = BT / WT;
   static constexpr int NW = NWR * NWT;
   static constexpr int NT = NW * kWave;
   static constexpr int MR = WR / 32, MT = WT / 32;        // 32x32 blocks per wave
-  static constexpr int ROWS = BR + BT;                     // rows per stage
-  static constexpr int RB = DMA ? 2 * KB : 2 * KB + 16;    // bytes per LDS row
-  static constexpr int STAGE_B = ROWS * RB;                // bytes per stage
-  static constexpr int DPW = ROWS * 2 * KB / 1024 / NW;    // 1 KB loads per wave per stage
-  static constexpr int MAIN_BYTES = (DMA ? NB : 2) * STAGE_B;
-  // small row tiles get extra LDS so the epilogue stages many segment runs at once
-  static constexpr int LDS_BYTES = MAIN_BYTES > 96 * 1024 ? MAIN_BYTES : 96 * 1024;
+  static constexpr int RB = 2 * KB;                        // bytes per LDS row
+  static constexpr int WSTAGE_B = BR * RB, XSTAGE_B = BT * RB;   // ring slots
+  static constexpr int DPW_W = BR * 2 * KB / 1024 / NW;    // 1 KB loads per wave per stage: W rows
+  static constexpr int DPW_X = BT * 2 * KB / 1024 / NW;    // and positions
+  static constexpr int DPW = DPW_W + DPW_X;
+  static constexpr int XRING = NB * WSTAGE_B;              // byte offset of the position ring
+  static constexpr int MAIN_BYTES = NB * WSTAGE_B + NX * XSTAGE_B;
+  // DMAs a wave has issued after stage st's position DMAs when stage st is
+  // multiplied (its W DMAs were issued earlier still)
+  static constexpr int VMC = (NX - 2) * DPW;
+  // small row tiles get extra LDS so the epilogue stages many segment runs at
+  // once; the y tile of the store passes through the same LDS
+  static constexpr int YT_BYTES = NW * WT * (2 * WR + 16);
+  static constexpr int LDS_BYTES0 = MAIN_BYTES > 96 * 1024 ? MAIN_BYTES : 96 * 1024;
+  static constexpr int LDS_BYTES = LDS_BYTES0 > YT_BYTES ? LDS_BYTES0 : YT_BYTES;
   static_assert(KB == 32 || KB == 64, "stage depth");
-  static_assert((ROWS * 2 * KB) % (1024 * NW) == 0, "a stage splits into whole loads per wave");
-  static_assert(NB >= 2 && (NB - 2) * DPW <= 63, "vmcnt range");
+  static_assert((BR * 2 * KB) % (1024 * NW) == 0 && (BT * 2 * KB) % (1024 * NW) == 0,
+                "each ring's stage splits into whole loads per wave");
+  static_assert(NB >= 2 && NX >= 2 && NB >= NX && VMC <= 63, "ring depths and vmcnt range");
 };
 
 template <int KB>
@@ -610,10 +619,10 @@ __device__ __forceinline__ void sched_reads_over_mfma() {
 
 // One workgroup per CU (the LDS stages take most of it): the register
 // allocator may then use the whole register file (waves_per_eu 1).
-template <int BR, int BT, int WR, int WT, int NB, int KB, bool DMA>
+template <int BR, int BT, int WR, int WT, int NB, int KB, int NX>
 __global__ __launch_bounds__((BR / WR) * (BT / WT) * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_gemm2(LinearArgs a) {
-  using C = GCfg<BR, BT, WR, WT, NB, KB, DMA>;
+  using C = GCfg<BR, BT, WR, WT, NB, KB, NX>;
   __shared__ __attribute__((aligned(1024))) uint16_t lds[C::LDS_BYTES / 2];
   __shared__ int4 pinfo[BT];
 
@@ -629,20 +638,19 @@ void k_gemm2(LinearArgs a) {
   const uint16_t* __restrict__ W = (const uint16_t*)a.W;
   const uint16_t* zeros = (const uint16_t*)a.pv.zeros;
 
-  // loader: load i of wave w fills the stage's 1 KB chunk J = i NW + w; lane
-  // l writes its byte J 1024 + 16 l, i.e. stage row r, slot l % (KB/8), and so
-  // fetches chunk (slot ^ swz(r)) of that row (W rows first, then the gathered
-  // rows of the tile's positions)
-  // (register path: piece q = tid + NT i is row q / (KB/8), chunk q % (KB/8),
-  // stored unswizzled at its padded place)
+  // loader: load i < DPW_W of wave w fills the W slot's 1 KB chunk
+  // J = i NW + w, load DPW_W + i the position slot's chunk J; lane l writes
+  // its byte J 1024 + 16 l of the slot, i.e. row r, slot l % (KB/8), and so
+  // fetches chunk (slot ^ swz(r)) of that row (W rows, or the gathered rows of
+  // the tile's positions)
   const uint16_t* src[C::DPW];
   int scol[C::DPW];
 #pragma unroll
   for (int i = 0; i < C::DPW; ++i) {
-    const int J = i * C::NW + wave;
-    const int q = tid + C::NT * i;
-    const int r = DMA ? J * (1024 / (2 * KB)) + lane / (KB / 8) : q / (KB / 8);
-    const int c = DMA ? (lane % (KB / 8)) ^ gswz<KB>(r) : q % (KB / 8);
+    const int J = (i >= C::DPW_W ? i - C::DPW_W : i) * C::NW + wave;
+    int r = J * (1024 / (2 * KB)) + lane / (KB / 8);
+    const int c = (lane % (KB / 8)) ^ gswz<KB>(r);
+    if (i >= C::DPW_W) r += BR;   // a row of the position slot
     scol[i] = c * 8;
     if (r < BR) {
       src[i] = W + (long long)min(r0 + r, d_out - 1) * d_in + c * 8;
@@ -654,20 +662,25 @@ void k_gemm2(LinearArgs a) {
     }
   }
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
-  // stage st -> ring slot st % NB; stages past d_in (and the k tail) read the
-  // zero block, so every stage issues the same DMA count and the ring's vmcnt
-  // waits stay exact
-  auto issue = [&](int st) {
+  // W rows of stage st -> W slot st % NB, positions -> position slot
+  // st % NX; stages past d_in (and the k tail) read the zero block, so every
+  // stage issues the same DMA count and the rings' vmcnt waits stay exact
+  auto issue_part = [&](int st, int i0, int n, uint32_t sb) {
     const int k0 = st * KB;
-    const uint32_t sb = lds0 + (uint32_t)(st % NB) * C::STAGE_B + (uint32_t)wave * 1024;
     if (k0 + KB <= d_in) {   // uniform: whole stage inside d_in
 #pragma unroll
-      for (int i = 0; i < C::DPW; ++i) dma16(src[i] + k0, sb + (uint32_t)i * C::NW * 1024);
+      for (int i = 0; i < n; ++i) dma16(src[i0 + i] + k0, sb + (uint32_t)i * C::NW * 1024);
     } else {
 #pragma unroll
-      for (int i = 0; i < C::DPW; ++i)
-        dma16(k0 + scol[i] < d_in ? src[i] + k0 : zeros, sb + (uint32_t)i * C::NW * 1024);
+      for (int i = 0; i < n; ++i)
+        dma16(k0 + scol[i0 + i] < d_in ? src[i0 + i] + k0 : zeros, sb + (uint32_t)i * C::NW * 1024);
     }
+  };
+  auto issue_w = [&](int st) {
+    issue_part(st, 0, C::DPW_W, lds0 + (uint32_t)(st % NB) * C::WSTAGE_B + (uint32_t)wave * 1024);
+  };
+  auto issue_x = [&](int st) {
+    issue_part(st, C::DPW_W, C::DPW_X, lds0 + C::XRING + (uint32_t)(st % NX) * C::XSTAGE_B + (uint32_t)wave * 1024);
   };
 
   f32x16_t acc[C::MR][C::MT];
@@ -682,18 +695,18 @@ void k_gemm2(LinearArgs a) {
   int fcol[KB / 16];
 #pragma unroll
   for (int kk = 0; kk < KB / 16; ++kk)
-    fcol[kk] = ((DMA ? (kk * 2 + kh / 8) ^ gswz<KB>(l32) : kk * 2 + kh / 8) * 16);
+    fcol[kk] = ((kk * 2 + kh / 8) ^ gswz<KB>(l32)) * 16;
   // the fragments of k-step kk + 1 are read while k-step kk is multiplied
-  auto compute = [&](int slot) {
-    const char* Ls = (const char*)lds + slot * C::STAGE_B;
+  // (Lw: the stage's W rows, Lx: its positions)
+  auto compute = [&](const char* Lw, const char* Lx) {
     u32x4_t af[2][C::MR], bf[2][C::MT];
     auto frag = [&](int kk, u32x4_t* fa, u32x4_t* fb) {
 #pragma unroll
       for (int m = 0; m < C::MR; ++m)
-        fa[m] = *(const u32x4_t*)(Ls + (wr * WR + m * 32 + l32) * C::RB + fcol[kk]);
+        fa[m] = *(const u32x4_t*)(Lw + (wr * WR + m * 32 + l32) * C::RB + fcol[kk]);
 #pragma unroll
       for (int n = 0; n < C::MT; ++n)
-        fb[n] = *(const u32x4_t*)(Ls + (BR + wt * WT + n * 32 + l32) * C::RB + fcol[kk]);
+        fb[n] = *(const u32x4_t*)(Lx + (wt * WT + n * 32 + l32) * C::RB + fcol[kk]);
     };
     frag(0, af[0], bf[0]);
 #pragma unroll
@@ -711,71 +724,29 @@ void k_gemm2(LinearArgs a) {
   };
 
   const int nst = (d_in + KB - 1) / KB;
-  if constexpr (DMA) {
-    // Ring: before stage st is multiplied, this wave's DMAs of stage st have
-    // landed (those of the NB - 2 later stages may still be in flight) and,
-    // past the barrier, so have every wave's; every wave is also done with
-    // stage st - 1, whose slot then takes stage st + NB - 1.
+  // Rings: iteration st requests the W rows of stage st + NB - 1, then the
+  // positions of stage st + NX - 1. Before stage st is multiplied, this
+  // wave's DMAs of stage st have landed (only those of later position
+  // stages and the W stages issued with them may still be in flight: VMC
+  // DMAs) and, past the barrier, so have every wave's; every wave is also
+  // done with stage st - 1, whose slots then take the new requests. The
+  // prologue issues the first stages in the same order the loop would.
+  const char* L = (const char*)lds;
 #pragma unroll
-    for (int st = 0; st < NB - 1; ++st) issue(st);
-    for (int st = 0; st < nst; ++st) {
-      vm_barrier<(NB - 2) * C::DPW>();
-      issue(st + NB - 1);
-      compute(st % NB);
-    }
-    // the ring's last DMAs (zero stages) land before the LDS is reused
-    vm_barrier<0>();
-  } else {
-    // PD stages of global loads in flight in a register ring (stage k in ring
-    // slot k % PD), two LDS slots. The stage count is padded to a multiple of
-    // PD: stages past d_in read the zero block and add nothing. Every load and
-    // store inside the loop is unconditional, so the compiler's vmcnt waits
-    // stay exact (a conditional load would make them drain the ring).
-    constexpr int PD = NB - 1;
-    u32x4_t stg[PD][C::DPW];
-    auto load = [&](int st, u32x4_t* r) {
-      const int k0 = st * KB;
+  for (int st = 0; st < NB - NX; ++st) issue_w(st);
 #pragma unroll
-      for (int i = 0; i < C::DPW; ++i) r[i] = ld16(k0 + scol[i] < d_in ? src[i] + k0 : zeros);
-    };
-    int sdst[C::DPW];
-#pragma unroll
-    for (int i = 0; i < C::DPW; ++i) {
-      const int q = tid + C::NT * i;
-      sdst[i] = q / (KB / 8) * C::RB + scol[i] * 2;
-    }
-    auto store = [&](int slot, const u32x4_t* r) {
-      char* Ls = (char*)lds + slot * C::STAGE_B;
-#pragma unroll
-      for (int i = 0; i < C::DPW; ++i) *(u32x4_t*)(Ls + sdst[i]) = r[i];
-    };
-    const int nst_pad = (nst + PD - 1) / PD * PD;
-    load(0, stg[0]);
-    store(0, stg[0]);
-#pragma unroll
-    for (int k = 1; k <= PD; ++k) load(k, stg[k % PD]);
-    __syncthreads();
-    for (int st0 = 0; st0 < nst_pad - PD; st0 += PD) {
-#pragma unroll
-      for (int u = 0; u < PD; ++u) {
-        const int st = st0 + u;
-        compute(st & 1);
-        store((st + 1) & 1, stg[(u + 1) % PD]);
-        load(st + 1 + PD, stg[(u + 1) % PD]);
-        __syncthreads();
-      }
-    }
-    {  // last PD stages: nothing further to prefetch
-      const int st0 = nst_pad - PD;
-#pragma unroll
-      for (int u = 0; u < PD; ++u) {
-        const int st = st0 + u;
-        compute(st & 1);
-        if (u + 1 < PD) store((st + 1) & 1, stg[(u + 1) % PD]);
-        __syncthreads();
-      }
-    }
+  for (int j = 0; j < NX - 1; ++j) {
+    issue_w(NB - NX + j);
+    issue_x(j);
   }
+  for (int st = 0; st < nst; ++st) {
+    vm_barrier<C::VMC>();
+    issue_w(st + NB - 1);
+    issue_x(st + NX - 1);
+    compute(L + (st % NB) * C::WSTAGE_B, L + C::XRING + (st % NX) * C::XSTAGE_B);
+  }
+  // the ring's last DMAs (zero stages) land before the LDS is reused
+  vm_barrier<0>();
 
   // ---- expand: acc += B_a (scale v) per segment run, on MFMA ---------------
   // scale*v of the tile's positions is staged in LDS (per rank chunk of up to
@@ -1038,11 +1009,11 @@ int shrink_items_bound(int T, int n_seg_bound) {
   return (n_seg_bound < kShrMaxSeg ? n_seg_bound : kShrMaxSeg) + (T + 63) / 64;
 }
 
-template <int BR, int BT, int WR, int WT, int NB, int KB, bool DMA>
+template <int BR, int BT, int WR, int WT, int NB, int KB, int NX>
 static void launch_g(const LinearArgs& a, hipStream_t st) {
   const int n_rt = (a.d_out + BR - 1) / BR, n_tt = (a.T + BT - 1) / BT;
-  hipLaunchKernelGGL((k_gemm2<BR, BT, WR, WT, NB, KB, DMA>), dim3(n_rt * n_tt),
-                     dim3(GCfg<BR, BT, WR, WT, NB, KB, DMA>::NT), 0, st, a);
+  hipLaunchKernelGGL((k_gemm2<BR, BT, WR, WT, NB, KB, NX>), dim3(n_rt * n_tt),
+                     dim3(GCfg<BR, BT, WR, WT, NB, KB, NX>::NT), 0, st, a);
 }
 
 // MLORA_FORCE_SHRINK=mfma keeps the MFMA shrink on short segments too.
@@ -1061,9 +1032,6 @@ bool shrink_short(const LinearArgs& a) {
          a.pv.max_rank <= 16 && shrink_short_enabled();
 }
 
-// Tile choice: large batches take 256x256 tiles (MFMA-bound, ~30 B/clk of L2
-// per CU); otherwise a tile spans every position of the batch (one read of x
-// per CU) with as few W rows as keep the CUs busy.
 void launch_shrink_bf16(const LinearArgs& a, hipStream_t st) {
   if (a.lora_on && a.seg_grid > 0) {
     // block counts of the shrink: ranks up to the pool's (at most 64 per
@@ -1095,16 +1063,25 @@ void launch_shrink_bf16(const LinearArgs& a, hipStream_t st) {
   }
 }
 
+// Tile choice: large batches take 256x256 tiles (MFMA-bound); otherwise
+// 128x128 tiles while they fill the GPU, else tiles that span 256 or 128
+// positions with 64 W rows. A measured sweep of tiles and ring depths on the
+// verify (256 tokens, 4096 -> 14336), heterogeneous (256 tokens,
+// 5120 -> 5120) and prefill (4096 tokens) shapes, every choice giving the
+// same bits: 128x128 tiles (3 W and 3 position slots) took the verify pass
+// from 53 to 48 us without LoRA; the 256x256 tile with 32-wide k-steps in
+// 3 + 3 LDS slots took the q projection from 158 to 144 us; the 64x128 tile
+// stayed best on the 5120-wide layer (deeper W rings gained nothing there).
 void launch_linear_bf16(const LinearArgs& a, hipStream_t st) {
   launch_shrink_bf16(a, st);
   auto tiles = [&](int br, int bt) {
     return (long long)((a.d_out + br - 1) / br) * ((a.T + bt - 1) / bt);
   };
   constexpr long long kFill = 192;   // tiles that keep most of the 256 CUs busy
-  if (a.T > 128 && tiles(256, 256) >= kFill) launch_g<256, 256, 128, 128, 2, 64, false>(a, st);
-  else if (a.T > 128 && tiles(128, 256) >= kFill) launch_g<128, 256, 64, 128, 2, 64, true>(a, st);
-  else if (a.T > 128 && tiles(64, 256) >= kFill) launch_g<64, 256, 64, 64, 3, 64, true>(a, st);
-  else launch_g<64, 128, 32, 64, 4, 64, true>(a, st);
+  if (a.T > 128 && tiles(256, 256) >= kFill) launch_g<256, 256, 128, 128, 3, 32, 3>(a, st);
+  else if (a.T > 64 && tiles(128, 128) >= kFill) launch_g<128, 128, 64, 64, 3, 64, 3>(a, st);
+  else if (a.T > 128 && tiles(64, 256) >= kFill) launch_g<64, 256, 64, 64, 3, 64, 3>(a, st);
+  else launch_g<64, 128, 32, 64, 4, 64, 4>(a, st);
 }
 
 }  // namespace mlora
