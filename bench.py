@@ -195,7 +195,9 @@ def shrink_split(case) -> int:
     if T <= 16 * nseg and case.max_rank <= 16:
         return 1
     groups = (case.d_in + 511) // 512
-    items = min(nseg, 16384) + (T + 63) // 64
+    # items: (block of 16 or 64 positions, group of 16 rank rows) per segment
+    pb = 64 if T > 16 * nseg else 16
+    items = (min(nseg, 16384) + (T + pb - 1) // pb) * max(1, (case.max_rank + 15) // 16)
     ks = 1
     while ks < 16 and ks * 2 <= groups and items * ks < 1024:
         ks *= 2

@@ -202,7 +202,7 @@ int run_linear(const void* x, const void* W, mlora_pool_s* pool, const SegView& 
     // writes the final scaled v and no finalize launch follows (measured
     // faster there; longer or higher-rank segments gain from the split)
     const bool one_chunk = lora_on && T <= 16 * a.seg_grid && pool->max_rank <= 16;
-    a.ks = one_chunk ? 1 : choose_shrink_split_bf16(pool->d_in, shrink_items_bound(T, a.seg_grid));
+    a.ks = one_chunk ? 1 : choose_shrink_split_bf16(pool->d_in, shrink_items_bound(T, a.seg_grid, pool->max_rank));
     if (fp == 3 && T <= 64) {
       if (log_calls())
         log_call("gemv", T, pool, sv, lora_on, a.ks, !lora_on || a.seg_grid <= 0 ? "none" : shrink_short(a) ? "short" : "mfma");

@@ -41,25 +41,24 @@ __device__ __forceinline__ f32x16_t mfma32g(u32x4_t a, u32x4_t b, f32x16_t c) {
 }
 
 // ---------------------------------------------------------------------------
-// Shrink. grid (items, d_in chunks), 4 waves. An item is one 64-position block
-// of one segment (segments longer than 64 positions give several items, so
-// long prefill segments spread over many workgroups); each workgroup finds
-// its item with a scan of the segment starts in LDS, where the segments'
-// adapter ids and ranks are loaded in the same round, so the A loads can
-// start right after the scan (the pool's slot table is read alongside and
-// only decides the per-position table). Chunk c covers k-steps
+// Shrink. grid (items, d_in chunks), 4 waves. An item is one block of 16 NRB
+// positions (one pass) of one segment times one group of 16 NCB rank rows
+// (longer segments or higher ranks give several items, so neither a long
+// segment nor a rank-64 adapter leaves one workgroup streaming all of its A);
+// each workgroup finds its item with a scan of the segment starts in LDS,
+// where the segments' adapter ids and ranks are loaded in the same round, so
+// the A loads can start right after the scan (the pool's slot table is read
+// alongside and only decides the per-position table). Chunk c covers k-steps
 // [c*nks/ks, (c+1)*nks/ks) of 32; wave w takes every fourth k-step starting
-// at w. A k-step loads NRB position blocks of x and NC rank blocks of A (16
-// each). The kernel is instantiated for the batch's position-block count and
-// its pool's largest rank (NCB blocks); each pass over a segment's rank rows
-// then takes the fewest blocks NC <= NCB that hold them, so a short, low-rank
-// segment keeps a deep ring of useful loads: 16 / (NRB + NC) k-steps of
-// operands in flight in registers (at most 64 operand VGPRs). Absent operands
-// read the pool's zero block (every load is unconditional, no loaded value
-// is selected). The four waves are summed in a fixed order through LDS into
-// v_part[c][p][j] (unscaled). MFMA rows = positions, columns = rank index.
+// at w. A k-step loads NRB position blocks of x and NC <= NCB rank blocks of
+// A (16 each): 16 / (NRB + NC) k-steps of operands in flight in registers (at
+// most 64 operand VGPRs). Absent operands read the pool's zero block (every
+// load is unconditional, no loaded value is selected). The four waves are
+// summed in a fixed order through LDS into v_part[c][p][j] (unscaled). MFMA
+// rows = positions, columns = rank index.
 // ---------------------------------------------------------------------------
 constexpr int kShrMaxSeg = MLORA_MAX_SEGMENTS;  // segments the item scan handles
+constexpr int kShrRankBlocks = 1;               // 16-row rank blocks per item (NCB)
 constexpr int kShrLdsSeg = 4096;                // up to this many, adapters and ranks go to LDS too
 
 // Whether the shrinks keep the segments' adapters and ranks in LDS next to
@@ -119,12 +118,21 @@ __global__ __launch_bounds__(256) void k_shrink2(LinearArgs a) {
   }
   if (tid == 0) found[0] = -1;
   __syncthreads();
+  // items of segment i: its blocks of 16 NRB positions (one pass each) times
+  // its groups of 16 NCB rank rows (at least one, which also writes the
+  // position table)
+  constexpr int PB = 16 * NRB;
+  auto n_items = [&](int i) {
+    const int len = min(sst[i + 1], T) - max(sst[i], 0);
+    if (len <= 0) return 0;
+    const int ad = meta_lds ? sad[i] : sv.seg_adapter[i];
+    const int rk = meta_lds ? srk[i] : (sv.seg_rank ? sv.seg_rank[i] : 0);
+    const int ra = ad >= 0 && ad < a.pv.capacity ? min(max(rk, 0), a.pv.max_rank) : 0;
+    return (len + PB - 1) / PB * max((ra + 16 * NCB - 1) / (16 * NCB), 1);
+  };
   const int per = (S + 255) / 256;
   int cnt = 0;
-  for (int i = tid * per; i < min(S, tid * per + per); ++i) {
-    const int len = min(sst[i + 1], T) - max(sst[i], 0);
-    cnt += len > 0 ? (len + 63) / 64 : 0;
-  }
+  for (int i = tid * per; i < min(S, tid * per + per); ++i) cnt += n_items(i);
   int inc = cnt;   // inclusive scan: wave, then the waves before it
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) {
@@ -139,8 +147,7 @@ __global__ __launch_bounds__(256) void k_shrink2(LinearArgs a) {
     if (item >= lo && item < inc) {
       int acc = lo;
       for (int i = tid * per; i < min(S, tid * per + per); ++i) {
-        const int len = min(sst[i + 1], T) - max(sst[i], 0);
-        const int nb = len > 0 ? (len + 63) / 64 : 0;
+        const int nb = n_items(i);
         if (item < acc + nb) {
           found[0] = i;
           found[1] = item - acc;
@@ -153,14 +160,18 @@ __global__ __launch_bounds__(256) void k_shrink2(LinearArgs a) {
   __syncthreads();
   const int s = found[0];
   if (s < 0) return;   // uniform: past the last item
-  const int ps = max(sst[s], 0) + 64 * found[1];
-  const int pe = min(min(sst[s + 1], T), ps + 64);
   // adapter and A rows to read: the segment's own id and rank, clamped into
   // the pool; the slot table (registration) is applied to the position table
   const int ad0 = meta_lds ? sad[s] : sv.seg_adapter[s];
   const int rk0 = meta_lds ? srk[s] : (sv.seg_rank ? sv.seg_rank[s] : 0);
   const bool adok = ad0 >= 0 && ad0 < a.pv.capacity;
   const int ra = adok ? min(max(rk0, 0), a.pv.max_rank) : 0;
+  const int ng = max((ra + 16 * NCB - 1) / (16 * NCB), 1);   // rank groups of the segment
+  const int pb = found[1] / ng, grp = found[1] % ng;
+  const int ps = max(sst[s], 0) + PB * pb;
+  const int pe = min(min(sst[s + 1], T), ps + PB);
+  const int jg0 = 16 * NCB * grp;                  // this item's rank rows [jg0, jg1)
+  const int jg1 = min(ra, jg0 + 16 * NCB);
   // The registered rank and the scale are only needed once the first sums
   // exist. Their loads are vector loads (offset vz is zero but held in a
   // vector register; a scalar load's wait would come with the next LDS wait),
@@ -180,7 +191,7 @@ __global__ __launch_bounds__(256) void k_shrink2(LinearArgs a) {
   // finalize launch follows.
   const bool fused = a.ks == 1;
   auto write_pos = [&]() {
-    if (c != 0) return;
+    if (c != 0 || grp != 0) return;   // once per position block
     resolve();
     const int ad = r_eff > 0 ? ad0 : -1;
     for (int p = ps + tid; p < pe; p += 256) a.pos_info[p] = make_int4(s, ad, r_eff, __float_as_int(r_eff > 0 ? scl : 0.f));
@@ -222,8 +233,8 @@ __global__ __launch_bounds__(256) void k_shrink2(LinearArgs a) {
       xrow[rb] = p < pe ? x + (long long)row * d_in : nullptr;
     }
     const int nrb = min(NRB, (pe - pg + 15) / 16);
-    for (int jg = 0; jg < ra; jg += 16 * NCB) {
-      const int ncb = min(NCB, (ra - jg + 15) / 16);
+    for (int jg = jg0; jg < jg1; jg += 16 * NCB) {   // (one pass: the item's rank group)
+      const int ncb = min(NCB, (jg1 - jg + 15) / 16);
       // one pass over rank columns [jg, jg + 16 NC): NC column blocks of 16
       // A rows are loaded per k-step. The pass takes the smallest NC that
       // holds the segment's rows, so a low-rank segment in a pool of a high
@@ -237,7 +248,7 @@ __global__ __launch_bounds__(256) void k_shrink2(LinearArgs a) {
 #pragma unroll
         for (int cb = 0; cb < NC; ++cb) {
           const int j = jg + cb * 16 + l16;
-          arow[cb] = j < ra ? Aa + (long long)j * d_in : nullptr;
+          arow[cb] = j < jg1 ? Aa + (long long)j * d_in : nullptr;
         }
         f32x4_t acc[NRB][NC];
 #pragma unroll
@@ -283,7 +294,7 @@ __global__ __launch_bounds__(256) void k_shrink2(LinearArgs a) {
             const float sum = ((red[0][l][q] + red[1][l][q]) + red[2][l][q]) + red[3][l][q];
             const int p = pg + rb * 16 + 4 * (l / 16) + v;
             const int j = jg + cb * 16 + (l % 16);
-            if (p < pe && j < ra) {
+            if (p < pe && j < jg1) {
               if (fused) a.v_fin[(long long)p * a.r_ws + j] = j < r_eff ? scl * sum : 0.f;
               else a.v_part[((long long)c * T + p) * a.r_ws + j] = sum;
             }
@@ -1005,8 +1016,13 @@ int choose_shrink_split_bf16(int d_in, int items) {
   return ks;
 }
 
-int shrink_items_bound(int T, int n_seg_bound) {
-  return (n_seg_bound < kShrMaxSeg ? n_seg_bound : kShrMaxSeg) + (T + 63) / 64;
+// items of the shrink: (block of 16 NRB positions, group of 16 NCB rank
+// rows) per segment; NRB = 4 when the mean segment is longer than 16
+// positions, else 1
+int shrink_items_bound(int T, int n_seg_bound, int max_rank) {
+  const int ng = (max_rank + 16 * kShrRankBlocks - 1) / (16 * kShrRankBlocks);
+  const int pb = T > 16 * n_seg_bound ? 64 : 16;
+  return ((n_seg_bound < kShrMaxSeg ? n_seg_bound : kShrMaxSeg) + (T + pb - 1) / pb) * (ng > 1 ? ng : 1);
 }
 
 template <int BR, int BT, int WR, int WT, int NB, int KB, int NX>
@@ -1034,12 +1050,11 @@ bool shrink_short(const LinearArgs& a) {
 
 void launch_shrink_bf16(const LinearArgs& a, hipStream_t st) {
   if (a.lora_on && a.seg_grid > 0) {
-    // block counts of the shrink: ranks up to the pool's (at most 64 per
-    // pass) and 16 or 64 positions per pass, by the batch's mean segment length
+    // the MFMA shrink takes 16 or 64 positions per pass, by the batch's mean
+    // segment length, and one group of 16 rank rows per item
     const int nseg = a.seg_grid < kShrMaxSeg ? a.seg_grid : kShrMaxSeg;
-    const int rmax = a.pv.max_rank < 64 ? a.pv.max_rank : 64;
     const bool long_segs = a.T > 16 * a.seg_grid;
-    const dim3 grid(shrink_items_bound(a.T, a.seg_grid), a.ks);
+    const dim3 grid(shrink_items_bound(a.T, a.seg_grid, a.pv.max_rank), a.ks);
     const size_t lds = shrink_lds_bytes(a.seg_grid);
     if (shrink_short(a)) {
       // at most two positions per segment on average, one d_in chunk, ranks <= 16
@@ -1047,15 +1062,8 @@ void launch_shrink_bf16(const LinearArgs& a, hipStream_t st) {
       hipLaunchKernelGGL(k_shrink_short, gs, dim3(256), lds, st, a);
       return;
     }
-    if (long_segs) {
-      if (rmax <= 16) hipLaunchKernelGGL((k_shrink2<4, 1>), grid, dim3(256), lds, st, a);
-      else if (rmax <= 32) hipLaunchKernelGGL((k_shrink2<4, 2>), grid, dim3(256), lds, st, a);
-      else hipLaunchKernelGGL((k_shrink2<4, 4>), grid, dim3(256), lds, st, a);
-    } else {
-      if (rmax <= 16) hipLaunchKernelGGL((k_shrink2<1, 1>), grid, dim3(256), lds, st, a);
-      else if (rmax <= 32) hipLaunchKernelGGL((k_shrink2<1, 2>), grid, dim3(256), lds, st, a);
-      else hipLaunchKernelGGL((k_shrink2<1, 4>), grid, dim3(256), lds, st, a);
-    }
+    if (long_segs) hipLaunchKernelGGL((k_shrink2<4, kShrRankBlocks>), grid, dim3(256), lds, st, a);
+    else hipLaunchKernelGGL((k_shrink2<1, kShrRankBlocks>), grid, dim3(256), lds, st, a);
     if (a.ks > 1) {
       const int n4 = a.T * (a.r_ws / 4);
       hipLaunchKernelGGL(k_vfinal, dim3((n4 + 255) / 256), dim3(256), 0, st, a);
