@@ -65,7 +65,8 @@ def parse():
                          "configuration under 'configs'; or one workload",
                     choices=["all", "decode_bf16", "verify_bf16", "hetero_bf16", "prefill_bf16", "tiny_f32",
                              "merge_bf16", "fused_qkv_decode", "fused_gateup_verify",
-                             "fused_qkv_prefill", "fused_gateup_prefill", "cycle_verify", "decode_fp8w"])
+                             "fused_qkv_prefill", "fused_gateup_prefill", "cycle_verify", "decode_fp8w",
+                             "path_sweep"])
     ap.add_argument("--proj", default="q", help="prefill projection (also the merge shape)")
     ap.add_argument("--rank", type=int, default=64, help="adapter rank of the merge workload")
     ap.add_argument("--rotate-gib", type=float, default=1.0)
@@ -80,6 +81,10 @@ def parse():
                     help="host only: turn the counter_collection.csv files of two --profile runs "
                          "(--pmc FETCH_SIZE, --pmc WRITE_SIZE) into the workload's entry of "
                          "profiles/traffic.json")
+    ap.add_argument("--sweep-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "MFMA_CSV"),
+                    help="host only, path_sweep: turn the counter_collection.csv files of three "
+                         "--profile runs (--pmc FETCH_SIZE, WRITE_SIZE, MfmaUtil) into per-call HBM "
+                         "bytes and MFMA utilisation per (tokens, path, pass)")
     return ap.parse_args()
 
 
@@ -535,6 +540,197 @@ def bench_cycle(args):
     print(json.dumps(out), flush=True)
 
 
+SWEEP_SHAPES = ((4096, 4096, (1, 2, 4, 8, 16, 32, 64, 128)),   # the decode batch's q projection
+                (4096, 14336, (16, 32, 48, 64, 128)))            # a wide gate/up projection
+SWEEP_PROFILE_CALLS = 3
+
+
+def sweep_plan():
+    """(d_out, tokens, path, lora_on) in the order the sweep runs them: the
+    split-K decode pair and the GEMV-style stream up to 64 tokens, the tiled
+    GEMM at every count."""
+    plan = []
+    for d_in, d_out, tokens in SWEEP_SHAPES:
+        for T in tokens:
+            for path in ("decode", "gemv", "gemm"):
+                if path != "gemm" and T > 64:
+                    continue
+                for lora_on in (1, 0):
+                    plan.append((d_out, T, path, lora_on))
+    return plan
+
+
+def sweep_case(d_in, d_out, T):
+    """The decode recipe at T tokens: d_in -> d_out, 32 rank-16 adapters
+    (scale 32 / 16), each token's adapter drawn uniformly at random and the
+    tokens grouped by adapter (sorted segments)."""
+    import numpy as np
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from mlora_inputs import make_custom_case
+    rng = np.random.default_rng(5000 + T)
+    tok = np.sort(rng.integers(0, 32, size=T).astype(np.int32), kind="stable")
+    return make_custom_case(5000 + T, "bf16", d_in, d_out, tok, {a: 16 for a in range(32)},
+                            scales={a: 2.0 for a in range(32)})
+
+
+def bench_path_sweep(args):
+    """Token-count sweep of the bf16 paths (decode pair, GEMV-style stream,
+    tiled GEMM), each forced in turn with MLORA_FORCE_PATH, LoRA-on and
+    LoRA-off, on the decode recipe at two layer shapes (SWEEP_SHAPES). With
+    --profile: a few calls per (shape, tokens, path, pass) in sweep_plan order
+    and one calibration copy, for rocprofv3 counter runs (--sweep-counters
+    reads them back)."""
+    import numpy as np
+    import torch
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import rank_adapter_gemm_segmented_amd as ml
+    from gpu_util import f32, i32, to_dev
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    prev = os.environ.get("MLORA_FORCE_PATH")
+    rows = []
+    try:
+        for d_in, d_out, tokens in SWEEP_SHAPES:
+            T_max = max(tokens)
+            base = sweep_case(d_in, d_out, T_max)
+            W0 = to_dev(base.W, "bf16")
+            x0 = to_dev(base.x, "bf16")
+            set_bytes = W0.numel() * 2 + 32 * 16 * (d_in + d_out) * 2
+            n_sets = 2 if args.profile else max(2, int(np.ceil(args.rotate_gib * (1 << 30) / set_bytes)))
+            sets = []
+            for i in range(n_sets):
+                pool = ml.Pool(d_in, d_out, torch.bfloat16, 16, 32)
+                for a in range(32):
+                    pool.register(a, to_dev(base.adapters[a].A, "bf16"), to_dev(base.adapters[a].B, "bf16"))
+                sets.append((W0 if i == 0 else W0.clone(), pool, pool.workspace(T_max),
+                             torch.empty((T_max, d_out), dtype=torch.bfloat16, device="cuda")))
+            metas = {}
+            for T in tokens:
+                c = sweep_case(d_in, d_out, T)
+                metas[T] = (i32(c.seg_start), i32(c.seg_adapter), i32(c.seg_rank), f32(c.seg_scale), int(c.n_seg))
+            torch.cuda.synchronize()
+
+            def step(i, T, lora_on):
+                W, pool, ws, y = sets[i % n_sets]
+                ss, sa, sr, sc, _ = metas[T]
+                ml.linear(x0[:T], W, pool, ss, sa, sr, sc, lora_on=lora_on, out=y[:T], workspace=ws)
+
+            for dout_p, T, path, lora_on in sweep_plan():
+                if dout_p != d_out:
+                    continue
+                os.environ["MLORA_FORCE_PATH"] = path
+                if args.profile:
+                    for i in range(SWEEP_PROFILE_CALLS):
+                        step(i, T, lora_on)
+                    torch.cuda.synchronize()
+                    continue
+                for i in range(args.warmup):
+                    step(i, T, lora_on)
+                torch.cuda.synchronize()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for i in range(args.warmup, args.warmup + args.steps):
+                    step(i, T, lora_on)
+                e1.record(stream)
+                e1.synchronize()
+                us = e0.elapsed_time(e1) / args.steps * 1e3
+                rows.append({"d_in": d_in, "d_out": d_out, "tokens": T, "path": path, "lora_on": lora_on,
+                             "us": round(us, 2), "segments": metas[T][4]})
+                print(f"[bench] sweep {d_in}->{d_out} T={T} {path} lora_on={lora_on}: {us:.2f} us",
+                      file=sys.stderr, flush=True)
+            del sets, W0, x0
+            torch.cuda.empty_cache()
+    finally:
+        if prev is None:
+            os.environ.pop("MLORA_FORCE_PATH", None)
+        else:
+            os.environ["MLORA_FORCE_PATH"] = prev
+    if args.profile:
+        n = CALIB_BYTES
+        src = torch.ones(n // 2, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] path sweep: {len(sweep_plan())} x {SWEEP_PROFILE_CALLS} calls, then a "
+              f"calibration copy of {n} bytes", file=sys.stderr, flush=True)
+        return
+    print(json.dumps({
+        "metric": "time per layer call by path and token count (decode recipe, two layer shapes)",
+        "unit": "us", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "higher_is_better": False, "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian weights, adapters and activations)",
+        "config": {"workload": "path_sweep", "shapes": [[a, b] for a, b, _ in SWEEP_SHAPES],
+                   "adapters": 32, "rank": 16},
+        "rows": rows}), flush=True)
+
+
+def ingest_sweep_counters(fetch_csv: str, write_csv: str, mfma_csv: str) -> list:
+    """Per (shape, tokens, path, pass): HBM bytes per call (FETCH_SIZE and WRITE_SIZE
+    scaled by the calibration copy, as ingest_counters does) and the
+    dispatch-weighted MfmaUtil of the call's kernels, from three --pmc runs
+    of `--workload path_sweep --profile`. The layer's dispatches are the
+    non-copy dispatches of each run, in sweep_plan order."""
+    import csv
+
+    def dispatches(path):
+        rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Dispatch_Id"]))
+        out = []
+        for r in rows:   # one row per (dispatch, counter); keep the first
+            if out and out[-1][0] == int(r["Dispatch_Id"]):
+                continue
+            out.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+        return out
+
+    res = {}
+    for key, path in (("fetch", fetch_csv), ("write", write_csv), ("mfma", mfma_csv)):
+        ds = dispatches(path)
+        copies = [d for d in ds if "rocclr" in d[1]]
+        layer = [d for d in ds if "rocclr" not in d[1] and "k_set_slot_rank" not in d[1]
+                 and "k_fill_u32" not in d[1]]
+        factor = 1.0
+        if key != "mfma":
+            calib = copies[-1][2] if copies else 0.0
+            if calib <= 0:
+                raise SystemExit(f"{path}: no calibration copy found")
+            factor = CALIB_BYTES / (calib * 1024.0)
+        res[key] = (layer, factor)
+    # a call's dispatches vary by path (decode pair, shrink + stream or GEMM,
+    # an optional fold): walk each run's layer dispatches call by call
+    out = []
+    pos = {"fetch": 0, "write": 0, "mfma": 0}
+    for d_out, T, path, lora_on in sweep_plan():
+        ent = {"d_out": d_out, "tokens": T, "path": path, "lora_on": lora_on}
+        for key in ("fetch", "write", "mfma"):
+            layer, factor = res[key]
+            vals, names = [], []
+            for c in range(SWEEP_PROFILE_CALLS):
+                # one call = the dispatches up to and including its last kernel
+                call = []
+                while True:
+                    d = layer[pos[key]]
+                    pos[key] += 1
+                    call.append(d)
+                    if _call_ends(d[1]):
+                        break
+                vals.append(call)
+                names = [re.search(r"k_\w+(<[^>]*>)?", d[1]).group(0) for d in call]
+            if key == "mfma":
+                ent["kernels"] = names
+                ent["mfma_util_pct"] = [round(sum(c[j][2] for c in vals) / len(vals), 2) for j in range(len(names))]
+            else:
+                tot = sum(sum(d[2] for d in c) for c in vals) / len(vals)
+                ent[f"{key}_mb"] = round(tot * 1024.0 * factor / 1e6, 3)
+        out.append(ent)
+    return out
+
+
+def _call_ends(kernel_name: str) -> bool:
+    """The last kernel of a layer call on each bf16 path."""
+    return any(k in kernel_name for k in ("k_finish_bf16", "k_gemv_bf16", "k_gemm2"))
+
+
 def bench_fp8w(args):
     """The decode batch with the base weight stored as FP8 e4m3 (per-row
     float32 scales) and bf16 adapters, LoRA-on and LoRA-off, over rotating
@@ -878,6 +1074,12 @@ def main():
         return
     if args.workload == "decode_fp8w":
         bench_fp8w(args)
+        return
+    if args.workload == "path_sweep":
+        if args.sweep_counters:
+            print(json.dumps({"path_sweep_counters": ingest_sweep_counters(*args.sweep_counters)}))
+            return
+        bench_path_sweep(args)
         return
 
     import torch

@@ -170,9 +170,13 @@ int run_linear(const void* x, const void* W, mlora_pool_s* pool, const SegView& 
   a.seg_grid = lora_on ? sv.n_seg : 0;
   if (pool->dtype == MLORA_BF16) {
     const int fp = forced_path();
-    // the split-K decode path up to 64 tokens, except on wide layers from 48
-    // tokens up, where the tiled GEMM measured faster (4096 -> 14336 at 48 and
-    // 64 tokens: LoRA-off 31 vs 44 us, LoRA-on equal)
+    // The split-K decode path up to 64 tokens, except on wide layers from 48
+    // tokens up; the tiled GEMM otherwise. Measured per path, token count and
+    // pass with HBM counters in profiles/path_sweep.txt: on 4096 -> 4096 the
+    // decode pair is the fastest LoRA-on path at 1-64 tokens (14.6-17.6 us,
+    // GEMM 39-48 us); on 4096 -> 14336 the GEMM wins from 48 tokens (48.2 vs
+    // 51.7 us LoRA-on, 31.8 vs 43.6 us LoRA-off). Both passes of a shape and
+    // token count take the same path, so a zero B reproduces the LoRA-off bits.
     const bool wide = T >= 48 && pool->d_out >= 8192;
     const bool dec_ok = decode_supported(T, lora_on ? sv.n_seg : 0, pool->d_out, pool->max_rank);
     if (w_scale || (dec_ok && (fp == 1 || (fp == 0 && !wide)))) {
