@@ -200,11 +200,13 @@ def shrink_split(case) -> int:
     if T <= 16 * nseg and case.max_rank <= 16:
         return 1
     groups = (case.d_in + 511) // 512
-    # items: (block of 16 or 64 positions, group of 16 rank rows) per segment
-    pb = 64 if T > 16 * nseg else 16
-    items = (min(nseg, 16384) + (T + pb - 1) // pb) * max(1, (case.max_rank + 15) // 16)
+    # items: (block of 16 NRB positions, group of 16 NCB rank rows) per
+    # segment; NRB = NCB = 4 for a mean segment longer than 16, else 1
+    long_segs = T > 16 * nseg
+    pb, ncb = (64, 4) if long_segs else (16, 1)
+    items = (min(nseg, 16384) + (T + pb - 1) // pb) * max(1, (case.max_rank + 16 * ncb - 1) // (16 * ncb))
     ks = 1
-    while ks < 16 and ks * 2 <= groups and items * ks < 1024:
+    while ks < 4 and ks * 2 <= groups and items * ks < 1024:
         ks *= 2
     return ks
 

@@ -58,7 +58,7 @@ __device__ __forceinline__ f32x16_t mfma32g(u32x4_t a, u32x4_t b, f32x16_t c) {
 // rows = positions, columns = rank index.
 // ---------------------------------------------------------------------------
 constexpr int kShrMaxSeg = MLORA_MAX_SEGMENTS;  // segments the item scan handles
-constexpr int kShrRankBlocks = 1;               // 16-row rank blocks per item (NCB)
+constexpr int kShrMaxSplit = 4;                 // d_in chunks of the MFMA shrink at most
 constexpr int kShrLdsSeg = 4096;                // up to this many, adapters and ranks go to LDS too
 
 // Whether the shrinks keep the segments' adapters and ranks in LDS next to
@@ -1007,21 +1007,33 @@ void k_gemm2(LinearArgs a) {
 // host side
 // ---------------------------------------------------------------------------
 // d_in chunks of the shrink: enough workgroups for the GPU, at most
-// kMaxShrinkSplit (the partials k_vfinal folds), each chunk at least one
+// kShrMaxSplit (the partials k_vfinal folds), each chunk at least one
 // 512-wide group.
 int choose_shrink_split_bf16(int d_in, int items) {
   const int groups = (d_in + 511) / 512;
   int ks = 1;
-  while (ks < kMaxShrinkSplit && ks * 2 <= groups && items * ks < 1024) ks *= 2;
+  while (ks < kShrMaxSplit && ks * 2 <= groups && items * ks < 1024) ks *= 2;
   return ks;
 }
 
+// Shapes of the MFMA shrink, by the batch's mean segment length (host
+// bound): longer than 16 positions, 64 positions per pass (NRB = 4) and all
+// of a segment's rank rows per item (NCB = 4: x is read once per position
+// block); otherwise 16 positions (NRB = 1) and 16 rank rows per item
+// (NCB = 1: a short segment of high rank spreads over several items).
+// Measured on the prefill (4096 tokens, 64 segments, rank 64) and
+// heterogeneous (256 tokens, ranks 8-64) batches: the prefill shrink took 30
+// us with NCB = 4 and 4 d_in chunks against 43 with NCB = 1 in one chunk;
+// the heterogeneous one 16.5 us with NCB = 1 in one chunk (more chunks or
+// rank blocks were slower).
+static bool shrink_long_segs(int T, int n_seg_bound) { return T > 16 * n_seg_bound; }
+
 // items of the shrink: (block of 16 NRB positions, group of 16 NCB rank
-// rows) per segment; NRB = 4 when the mean segment is longer than 16
-// positions, else 1
+// rows) per segment
 int shrink_items_bound(int T, int n_seg_bound, int max_rank) {
-  const int ng = (max_rank + 16 * kShrRankBlocks - 1) / (16 * kShrRankBlocks);
-  const int pb = T > 16 * n_seg_bound ? 64 : 16;
+  const int ncb = shrink_long_segs(T, n_seg_bound) ? 4 : 1;
+  const int ng = (max_rank + 16 * ncb - 1) / (16 * ncb);
+  const int pb = shrink_long_segs(T, n_seg_bound) ? 64 : 16;
   return ((n_seg_bound < kShrMaxSeg ? n_seg_bound : kShrMaxSeg) + (T + pb - 1) / pb) * (ng > 1 ? ng : 1);
 }
 
@@ -1050,10 +1062,10 @@ bool shrink_short(const LinearArgs& a) {
 
 void launch_shrink_bf16(const LinearArgs& a, hipStream_t st) {
   if (a.lora_on && a.seg_grid > 0) {
-    // the MFMA shrink takes 16 or 64 positions per pass, by the batch's mean
-    // segment length, and one group of 16 rank rows per item
+    // the MFMA shrink's shape follows the batch's mean segment length
+    // (shrink_long_segs)
     const int nseg = a.seg_grid < kShrMaxSeg ? a.seg_grid : kShrMaxSeg;
-    const bool long_segs = a.T > 16 * a.seg_grid;
+    const bool long_segs = shrink_long_segs(a.T, a.seg_grid);
     const dim3 grid(shrink_items_bound(a.T, a.seg_grid, a.pv.max_rank), a.ks);
     const size_t lds = shrink_lds_bytes(a.seg_grid);
     if (shrink_short(a)) {
@@ -1062,8 +1074,8 @@ void launch_shrink_bf16(const LinearArgs& a, hipStream_t st) {
       hipLaunchKernelGGL(k_shrink_short, gs, dim3(256), lds, st, a);
       return;
     }
-    if (long_segs) hipLaunchKernelGGL((k_shrink2<4, kShrRankBlocks>), grid, dim3(256), lds, st, a);
-    else hipLaunchKernelGGL((k_shrink2<1, kShrRankBlocks>), grid, dim3(256), lds, st, a);
+    if (long_segs) hipLaunchKernelGGL((k_shrink2<4, 4>), grid, dim3(256), lds, st, a);
+    else hipLaunchKernelGGL((k_shrink2<1, 1>), grid, dim3(256), lds, st, a);
     if (a.ks > 1) {
       const int n4 = a.T * (a.r_ws / 4);
       hipLaunchKernelGGL(k_vfinal, dim3((n4 + 255) / 256), dim3(256), 0, st, a);
@@ -1079,7 +1091,11 @@ void launch_shrink_bf16(const LinearArgs& a, hipStream_t st) {
 // same bits: 128x128 tiles (3 W and 3 position slots) took the verify pass
 // from 53 to 48 us without LoRA; the 256x256 tile with 32-wide k-steps in
 // 3 + 3 LDS slots took the q projection from 158 to 144 us; the 64x128 tile
-// stayed best on the 5120-wide layer (deeper W rings gained nothing there).
+// stayed best on the 5120-wide layer (deeper W rings gained nothing there),
+// its waves split by positions (64 rows x 32 positions each): a wave then
+// walks the segment runs of 32 positions, not 64, in units of 2 KB of B
+// rather than 1 KB, and the heterogeneous batch's LoRA-on call dropped from
+// 98 to 88 us.
 void launch_linear_bf16(const LinearArgs& a, hipStream_t st) {
   launch_shrink_bf16(a, st);
   auto tiles = [&](int br, int bt) {
@@ -1089,7 +1105,7 @@ void launch_linear_bf16(const LinearArgs& a, hipStream_t st) {
   if (a.T > 128 && tiles(256, 256) >= kFill) launch_g<256, 256, 128, 128, 3, 32, 3>(a, st);
   else if (a.T > 64 && tiles(128, 128) >= kFill) launch_g<128, 128, 64, 64, 3, 64, 3>(a, st);
   else if (a.T > 128 && tiles(64, 256) >= kFill) launch_g<64, 256, 64, 64, 3, 64, 3>(a, st);
-  else launch_g<64, 128, 32, 64, 4, 64, 4>(a, st);
+  else launch_g<64, 128, 64, 32, 4, 64, 4>(a, st);
 }
 
 }  // namespace mlora

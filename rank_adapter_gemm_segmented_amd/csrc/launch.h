@@ -88,7 +88,7 @@ void launch_shrink_bf16(const LinearArgs& a, hipStream_t st);
 // full-d_in GEMV with the expand for T <= 64 (kernels_gemv.hip); LoRA-on
 // needs launch_shrink_bf16 first
 void launch_gemv_bf16(const LinearArgs& a, hipStream_t st);
-int choose_shrink_split_bf16(int d_in, int seg_grid);
+int choose_shrink_split_bf16(int d_in, int items);
 int shrink_items_bound(int T, int n_seg_bound, int max_rank);
 // true when the shrink of this call is k_shrink_short (else k_shrink2)
 bool shrink_short(const LinearArgs& a);
