@@ -70,6 +70,9 @@ def parse():
     ap.add_argument("--proj", default="q", help="prefill projection (also the merge shape)")
     ap.add_argument("--rank", type=int, default=64, help="adapter rank of the merge workload")
     ap.add_argument("--rotate-gib", type=float, default=1.0)
+    ap.add_argument("--clock-warmup", type=float, default=0.5,
+                    help="seconds of untimed sustained load before each workload's warm-up and "
+                         "timed calls (the GPU's clocks ramp under load)")
     ap.add_argument("--graph", action="store_true",
                     help="time the K calls as HIP-graph replays (eager times are reported too)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -943,6 +946,7 @@ def measure_layer(case, args, label: str):
         torch.cuda.synchronize()
         print(f"[bench] calibration copy of {n} bytes done", file=sys.stderr, flush=True)
         return res
+    clock_warmup(lambda: (step(rot[0], 1), rot.__setitem__(0, rot[0] + 1)), args.clock_warmup)
     res["ms_on_eager"] = timed(1, args.steps, args.warmup)
     res["ms_off_eager"] = timed(0, args.steps, args.warmup)
     res["ms_on"], res["ms_off"] = res["ms_on_eager"], res["ms_off_eager"]
@@ -958,6 +962,22 @@ def measure_layer(case, args, label: str):
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return res
+
+
+def clock_warmup(call, seconds: float):
+    """Untimed sustained load before a workload's timed calls: measured on
+    the box, the same kernel ran up to 15% slower in the first ~100 ms of
+    load (the GPU's clocks ramp), so a short timed loop after an idle host
+    phase would read low. Runs `call` back to back for `seconds`."""
+    import torch
+    t_end = time.time() + seconds
+    n = 0
+    while time.time() < t_end:
+        call()
+        n += 1
+        if n % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
 
 
 def layer_summary(case, res, args) -> dict:
@@ -1127,7 +1147,8 @@ def main():
         "byte_floor_ratio": round(bytes_on / bytes_off, 4),
         "timing": ("K calls replayed from HIP graphs (one graph per pass over the buffer sets)"
                    if args.graph else "K eager calls through the Python binding, buffer sets rotated "
-                   "continuously from the warm-up on"),
+                   "continuously from the warm-up on")
+                  + f"; each workload first runs {args.clock_warmup} s of untimed LoRA-on calls (clock ramp)",
         "eager": {"ms_per_step_lora_on": round(res["ms_on_eager"], 6),
                   "ms_per_step_lora_off": round(res["ms_off_eager"], 6)},
         "roofline": summ["roofline"],

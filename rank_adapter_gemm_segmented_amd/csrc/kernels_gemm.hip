@@ -629,9 +629,11 @@ __device__ __forceinline__ void sched_reads_over_mfma() {
 }
 
 // One workgroup per CU (the LDS stages take most of it): the register
-// allocator may then use the whole register file (waves_per_eu 1).
+// allocator may then use the whole register file share of its waves (one
+// wave per SIMD for 4 waves, two for 8).
 template <int BR, int BT, int WR, int WT, int NB, int KB, int NX>
-__global__ __launch_bounds__((BR / WR) * (BT / WT) * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__((BR / WR) * (BT / WT) * kWave)
+__attribute__((amdgpu_waves_per_eu((BR / WR) * (BT / WT) / 4, (BR / WR) * (BT / WT) / 4)))
 void k_gemm2(LinearArgs a) {
   using C = GCfg<BR, BT, WR, WT, NB, KB, NX>;
   __shared__ __attribute__((aligned(1024))) uint16_t lds[C::LDS_BYTES / 2];
@@ -1089,8 +1091,10 @@ void launch_shrink_bf16(const LinearArgs& a, hipStream_t st) {
 // verify (256 tokens, 4096 -> 14336), heterogeneous (256 tokens,
 // 5120 -> 5120) and prefill (4096 tokens) shapes, every choice giving the
 // same bits: 128x128 tiles (3 W and 3 position slots) took the verify pass
-// from 53 to 48 us without LoRA; the 256x256 tile with 32-wide k-steps in
-// 3 + 3 LDS slots took the q projection from 158 to 144 us; the 64x128 tile
+// from 53 to 48 us without LoRA; the 256x256 tile with 8 waves (two per
+// SIMD, 128 rows x 64 positions each), 32-wide k-steps and double-buffered
+// LDS slots took the q projection from 158 to 135-139 us (4 waves with 3 + 3
+// slots: 142-144 us, after a sustained warm-up in both); the 64x128 tile
 // stayed best on the 5120-wide layer (deeper W rings gained nothing there),
 // its waves split by positions (64 rows x 32 positions each): a wave then
 // walks the segment runs of 32 positions, not 64, in units of 2 KB of B
@@ -1102,7 +1106,7 @@ void launch_linear_bf16(const LinearArgs& a, hipStream_t st) {
     return (long long)((a.d_out + br - 1) / br) * ((a.T + bt - 1) / bt);
   };
   constexpr long long kFill = 192;   // tiles that keep most of the 256 CUs busy
-  if (a.T > 128 && tiles(256, 256) >= kFill) launch_g<256, 256, 128, 128, 3, 32, 3>(a, st);
+  if (a.T > 128 && tiles(256, 256) >= kFill) launch_g<256, 256, 128, 64, 2, 32, 2>(a, st);
   else if (a.T > 64 && tiles(128, 128) >= kFill) launch_g<128, 128, 64, 64, 3, 64, 3>(a, st);
   else if (a.T > 128 && tiles(64, 256) >= kFill) launch_g<64, 256, 64, 64, 3, 64, 3>(a, st);
   else launch_g<64, 128, 64, 32, 4, 64, 4>(a, st);
