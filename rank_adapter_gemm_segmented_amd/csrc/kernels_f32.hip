@@ -9,7 +9,8 @@
 
 namespace mlora {
 
-// v_part[0][p][j] = sum_k A_a[j,k] x[row(p),k]; one workgroup per segment.
+// v_part[0][p][j] = sum_k A_a[j,k] x[row(p),k]; one workgroup per segment,
+// which also writes its positions' entries of the position table.
 // Wave w takes positions ps + w, ps + w + 4, ...; for a position, groups of
 // kF32Rows rank rows are read together (every load of the group in flight),
 // the 64 lanes splitting d_in (16-byte loads, lane l at k = 4l + 256 i); each
@@ -27,6 +28,9 @@ __global__ __launch_bounds__(256) void k_shrink_f32(LinearArgs a) {
   if (pe <= ps) return;
   int r;
   const int ad = seg_adapter_checked(sv, a.pv, s, &r);
+  // the position table: {segment, adapter or -1, rank, scale bits}
+  for (int p = ps + (int)threadIdx.x; p < pe; p += 256)
+    a.pos_info[p] = make_int4(s, ad, ad >= 0 ? r : 0, __float_as_int(ad >= 0 ? sv.seg_scale[s] : 0.f));
   if (ad < 0) return;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const float* __restrict__ x = (const float*)a.x;
@@ -65,101 +69,94 @@ __global__ __launch_bounds__(256) void k_shrink_f32(LinearArgs a) {
   }
 }
 
-// Tile: 64 output features x 16 sorted positions; thread (tx, ty) owns feature
-// n0+tx for positions 4*ty .. 4*ty+3. d_in is walked in chunks of kF32KB with
-// the next chunk's loads in flight in registers while the current one is
-// multiplied from LDS.
-constexpr int kF32KB = 64;
+// Tile: 16 output features x 16 sorted positions, one output per thread
+// (tx = feature, ty = position), so a small layer spreads over many
+// workgroups: the 256-wide layer of 16 tokens runs 16 of them (64-feature
+// tiles ran 4, each issuing ~5000 LDS reads per wave: 10 us). d_in is walked
+// in chunks of kF32KB columns with the next chunk's loads in flight in
+// registers while the current one is multiplied from LDS; the chunk is wide
+// (4 W and 4 x loads of 16 bytes per thread, all in flight at once), so a
+// small layer loads everything in one round trip.
+constexpr int kF32KB = 256;
+constexpr int kF32Feat = 16;
 
 __global__ __launch_bounds__(256) void k_gemm_f32(LinearArgs a) {
-  __shared__ float Ws[64][kF32KB + 1];
+  __shared__ float Ws[kF32Feat][kF32KB + 1];
   __shared__ float Xs[16][kF32KB + 1];
   const int tid = threadIdx.x;
-  const int tx = tid % 64, ty = tid / 64;
-  const int n0 = blockIdx.x * 64, p0 = blockIdx.y * 16;
+  const int tx = tid % kF32Feat, ty = tid / kF32Feat;
+  const int n0 = blockIdx.x * kF32Feat, p0 = blockIdx.y * 16;
   const int T = a.T, d_in = a.d_in, d_out = a.d_out;
   const float* __restrict__ x = (const float*)a.x;
   const float* __restrict__ W = (const float*)a.W;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-
-  // loader: W chunk 64 x 64 = 1024 float4 (4 per thread), x chunk 16 x 64 =
-  // 256 float4 (1 per thread); absent rows or columns load zeros
-  const float* wsrc[4];
-  int wr_[4], wc_[4];
+  float acc = 0.f;
+  // loader: W chunk 16 x 256 and x chunk 16 x 256, 1024 float4 each (4 per
+  // thread); absent rows or columns load zeros
+  constexpr int N4 = 16 * kF32KB / 4 / 256;
+  const float* wsrc[N4];
+  const float* xsrc[N4];
+  int lr_[N4], lc_[N4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < N4; ++i) {
     const int q = tid + 256 * i;
-    wr_[i] = q / (kF32KB / 4);
-    wc_[i] = 4 * (q % (kF32KB / 4));
-    wsrc[i] = W + (long long)min(n0 + wr_[i], d_out - 1) * d_in + wc_[i];
+    lr_[i] = q / (kF32KB / 4);
+    lc_[i] = 4 * (q % (kF32KB / 4));
+    wsrc[i] = W + (long long)min(n0 + lr_[i], d_out - 1) * d_in + lc_[i];
+    int xrow = min(p0 + lr_[i], T - 1);
+    if (a.sv.token_index) xrow = min(max(a.sv.token_index[xrow], 0), T - 1);
+    xsrc[i] = x + (long long)xrow * d_in + lc_[i];
   }
-  const int xr_ = tid / (kF32KB / 4), xc_ = 4 * (tid % (kF32KB / 4));
-  int xrow = min(p0 + xr_, T - 1);
-  if (a.sv.token_index) xrow = min(max(a.sv.token_index[xrow], 0), T - 1);
-  const float* xsrc = x + (long long)xrow * d_in + xc_;
-  f32x4_t wreg[4], xreg;
+  // this position's adapter entry, requested with the first chunk (the
+  // epilogue's B and v loads then need no further round trip)
+  const int p = p0 + ty;
+  const int4 pe4 = a.lora_on ? a.pos_info[min(p, T - 1)] : make_int4(0, -1, 0, 0);
+  f32x4_t wreg[N4], xreg[N4];
   auto load = [&](int kb) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool ok = n0 + wr_[i] < d_out && kb + wc_[i] < d_in;
-      wreg[i] = ok ? *(const f32x4_t*)(wsrc[i] + kb) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < N4; ++i) {
+      const bool wok = n0 + lr_[i] < d_out && kb + lc_[i] < d_in;
+      wreg[i] = wok ? *(const f32x4_t*)(wsrc[i] + kb) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const bool xok = p0 + lr_[i] < T && kb + lc_[i] < d_in;
+      xreg[i] = xok ? *(const f32x4_t*)(xsrc[i] + kb) : f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    const bool ok = p0 + xr_ < T && kb + xc_ < d_in;
-    xreg = ok ? *(const f32x4_t*)(xsrc + kb) : f32x4_t{0.f, 0.f, 0.f, 0.f};
   };
   load(0);
   for (int kb = 0; kb < d_in; kb += kF32KB) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < N4; ++i)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) Ws[wr_[i]][wc_[i] + c] = wreg[i][c];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) Xs[xr_][xc_ + c] = xreg[c];
+      for (int c = 0; c < 4; ++c) {
+        Ws[lr_[i]][lc_[i] + c] = wreg[i][c];
+        Xs[lr_[i]][lc_[i] + c] = xreg[i][c];
+      }
     __syncthreads();
     if (kb + kF32KB < d_in) load(kb + kF32KB);   // uniform
 #pragma unroll 16
-    for (int kk = 0; kk < kF32KB; ++kk) {
-      const float w = Ws[tx][kk];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) acc[q] = fmaf(w, Xs[ty * 4 + q][kk], acc[q]);
-    }
+    for (int kk = 0; kk < kF32KB; ++kk) acc = fmaf(Ws[tx][kk], Xs[ty][kk], acc);
     __syncthreads();
   }
-
   const int n = n0 + tx;
-  if (n >= d_out) return;
+  if (n >= d_out || p >= T) return;
   const SegView& sv = a.sv;
-  const int S = a.lora_on ? seg_count(sv) : 0;
-  float* __restrict__ y = (float*)a.y;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int p = p0 + ty * 4 + q;
-    if (p >= T) continue;
-    float val = acc[q];
-    if (S > 0) {
-      const int s = find_segment(sv.seg_start, S, p);
-      int r;
-      const int ad = (sv.seg_start[s] <= p && p < sv.seg_start[s + 1])
-                         ? seg_adapter_checked(sv, a.pv, s, &r) : -1;
-      if (ad >= 0) {
-        const float* Bb = (const float*)a.pv.base + (long long)ad * a.pv.slot_elems + a.pv.b_offset;
-        const float* bn = Bb + (long long)n * round_up8(r);
-        const float* vp = a.v_part + (long long)p * a.r_ws;
-        float lora = 0.f;
-        for (int j = 0; j < r; ++j) lora = fmaf(bn[j], vp[j], lora);
-        val = fmaf(sv.seg_scale[s], lora, val);
-      }
-    }
-    int row = sv.token_index ? sv.token_index[p] : p;
-    row = min(max(row, 0), T - 1);
-    y[(long long)row * d_out + n] = val;
+  float val = acc;
+  const int ad = pe4.y, r = min(pe4.z, a.pv.max_rank);
+  if (a.lora_on && ad >= 0 && ad < a.pv.capacity && r > 0) {
+    const float* Bb = (const float*)a.pv.base + (long long)ad * a.pv.slot_elems + a.pv.b_offset;
+    const float* bn = Bb + (long long)n * round_up8(r);
+    const float* vp = a.v_part + (long long)p * a.r_ws;
+    float lora = 0.f;
+    for (int j = 0; j < r; ++j) lora = fmaf(bn[j], vp[j], lora);
+    val = fmaf(__int_as_float(pe4.w), lora, val);
   }
+  int row = sv.token_index ? sv.token_index[p] : p;
+  row = min(max(row, 0), T - 1);
+  ((float*)a.y)[(long long)row * d_out + n] = val;
 }
 
 void launch_linear_f32(const LinearArgs& a, hipStream_t st) {
   if (a.lora_on && a.seg_grid > 0)
     hipLaunchKernelGGL(k_shrink_f32, dim3(a.seg_grid), dim3(256), 0, st, a);
-  dim3 grid((a.d_out + 63) / 64, (a.T + 15) / 16);
+  dim3 grid((a.d_out + kF32Feat - 1) / kF32Feat, (a.T + 15) / 16);
   hipLaunchKernelGGL(k_gemm_f32, grid, dim3(256), 0, st, a);
 }
 
