@@ -13,8 +13,8 @@
 //             segments of rank <= 16 (vector-ALU dot products, real rows only).
 //  k_gemm2    W x as a tiled GEMM on v_mfma_f32_32x32x16_bf16: block tile of
 //             BR W rows x BT sorted positions over the whole of d_in, both
-//             operands staged through LDS (a direct-to-LDS load ring on the
-//             narrow tiles, register staging on the 256x256 one). The
+//             operands staged through LDS by direct-to-LDS loads (a ring of
+//             NB W stages and one of NX position stages). The
 //             epilogue adds scale * B_a v on the same accumulators with MFMAs
 //             (v split into a bf16 high and low part, ~16 mantissa bits) and
 //             stores y once, through an LDS transpose.
