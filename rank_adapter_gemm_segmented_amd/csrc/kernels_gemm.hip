@@ -584,8 +584,8 @@ __device__ __forceinline__ void vm_barrier() {
 // positions over KB columns. The stages reach LDS by direct loads into two
 // rings, one for the W rows (NB slots, NB - 1 stages in flight while one is
 // multiplied) and one for the positions (NX slots, NX - 1 in flight). Rows
-// are 2 KB bytes, unpadded, and 16-byte chunk c of row r sits in slot
-// c ^ swz(r) of the row, so the rows read together by one fragment load fall
+// are 2 KB bytes (KB bf16), unpadded, and 16-byte chunk c of row r sits in slot
+// c ^ gswz(r) of the row, so the rows read together by one fragment load fall
 // in distinct LDS banks.
 template <int BR, int BT, int WR, int WT, int NB, int KB, int NX>
 struct GCfg {
@@ -614,8 +614,19 @@ struct GCfg {
   static_assert(NB >= 2 && NX >= 2 && NB >= NX && VMC <= 63, "ring depths and vmcnt range");
 };
 
+// Slot permutation of row r (depends on r mod 16 only). A fragment read has
+// lane l take row l % 32 at one chunk. gfx950 serves a 16-byte LDS read 16
+// lanes (256 bytes) at a time, so the 16 rows of a lane group must land on
+// 16 distinct 16-byte bank groups modulo 256 bytes. KB = 64: two rows per
+// 256 bytes; rows of equal parity take distinct slots through r >> 1, and
+// the parity flips the slot's top bit. KB = 32: four rows per 256 bytes,
+// separated through r >> 2. Both were checked with the LDS bank-conflict
+// counter on a read-pattern probe (no conflicts), where the plain r & 7 and
+// (r >> 1) & 3 permutations conflicted two ways.
 template <int KB>
-__device__ __forceinline__ int gswz(int r) { return KB == 64 ? (r & 7) : ((r >> 1) & 3); }
+__device__ __forceinline__ int gswz(int r) {
+  return KB == 64 ? (((r >> 1) ^ ((r & 1) << 2)) & 7) : ((r >> 2) & 3);
+}
 
 // Scheduling hint for one k-step: the R fragment reads of the next k-step
 // spread over the M MFMAs of this one (one read, then its share of MFMAs).
@@ -654,7 +665,7 @@ void k_gemm2(LinearArgs a) {
   // loader: load i < DPW_W of wave w fills the W slot's 1 KB chunk
   // J = i NW + w, load DPW_W + i the position slot's chunk J; lane l writes
   // its byte J 1024 + 16 l of the slot, i.e. row r, slot l % (KB/8), and so
-  // fetches chunk (slot ^ swz(r)) of that row (W rows, or the gathered rows of
+  // fetches chunk (slot ^ gswz(r)) of that row (W rows, or the gathered rows of
   // the tile's positions)
   const uint16_t* src[C::DPW];
   int scol[C::DPW];
@@ -1091,22 +1102,24 @@ void launch_shrink_bf16(const LinearArgs& a, hipStream_t st) {
 // verify (256 tokens, 4096 -> 14336), heterogeneous (256 tokens,
 // 5120 -> 5120) and prefill (4096 tokens) shapes, every choice giving the
 // same bits: 128x128 tiles (3 W and 3 position slots) took the verify pass
-// from 53 to 48 us without LoRA; the 256x256 tile with 8 waves (two per
-// SIMD, 128 rows x 64 positions each), 32-wide k-steps and double-buffered
-// LDS slots took the q projection from 158 to 135-139 us (4 waves with 3 + 3
-// slots: 142-144 us, after a sustained warm-up in both); the 64x128 tile
-// stayed best on the 5120-wide layer (deeper W rings gained nothing there),
-// its waves split by positions (64 rows x 32 positions each): a wave then
-// walks the segment runs of 32 positions, not 64, in units of 2 KB of B
-// rather than 1 KB, and the heterogeneous batch's LoRA-on call dropped from
-// 98 to 88 us.
+// from 53 to 48 us without LoRA (4 + 4 slots, or 32-wide stages in rings of
+// 6-9, were slower); the 256x256 tile runs 8 waves (two per SIMD, 128 rows x
+// 64 positions each) on 64-wide stages in 2 + 2 slots: against 32-wide
+// stages in 2 + 2 slots it took the q projection from 211 to 197 us with
+// LoRA and 155 to 150 without, gate/up from 597 to 548 and 501 to 443, down
+// from 573 to 504 and 495 to 411 (32-wide stages in rings of 3-6 slots were
+// in between); the 64x128 tile stayed best on the 5120-wide layer (deeper
+// W rings gained nothing there), its waves split by positions (64 rows x 32
+// positions each): a wave then walks the segment runs of 32 positions, not
+// 64, in units of 2 KB of B rather than 1 KB, and the heterogeneous batch's
+// LoRA-on call dropped from 98 to 88 us.
 void launch_linear_bf16(const LinearArgs& a, hipStream_t st) {
   launch_shrink_bf16(a, st);
   auto tiles = [&](int br, int bt) {
     return (long long)((a.d_out + br - 1) / br) * ((a.T + bt - 1) / bt);
   };
   constexpr long long kFill = 192;   // tiles that keep most of the 256 CUs busy
-  if (a.T > 128 && tiles(256, 256) >= kFill) launch_g<256, 256, 128, 64, 2, 32, 2>(a, st);
+  if (a.T > 128 && tiles(256, 256) >= kFill) launch_g<256, 256, 128, 64, 2, 64, 2>(a, st);
   else if (a.T > 64 && tiles(128, 128) >= kFill) launch_g<128, 128, 64, 64, 3, 64, 3>(a, st);
   else if (a.T > 128 && tiles(64, 256) >= kFill) launch_g<64, 256, 64, 64, 3, 64, 3>(a, st);
   else launch_g<64, 128, 64, 32, 4, 64, 4>(a, st);
