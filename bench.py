@@ -214,12 +214,27 @@ def shrink_split(case) -> int:
     return ks
 
 
+def dense_expand(case):
+    """Whether the library adds the adapter term as a dense fp32 tile
+    (k_expand_delta) rather than in the GEMM epilogue (api.hip,
+    use_dense_expand): plain bf16 pools of largest rank 32..64, d_out a
+    multiple of 8, at most 512 tokens and 16 MiB of term; MLORA_EXPAND=dense
+    or mfma forces either where eligible."""
+    T, d_out, r = case.n_tokens, case.d_out, case.max_rank
+    ok = (case.dtype == "bf16" and r <= 64 and d_out % 8 == 0 and T <= 512 and T * d_out * 4 <= (16 << 20))
+    mode = os.environ.get("MLORA_EXPAND")
+    if not ok or mode == "mfma":
+        return False
+    return mode == "dense" or r >= 32
+
+
 def layer_kernels(case):
     """Kernels of one LoRA-on layer call, run back to back on one stream: the
     split-K stream + finish pair for T <= 64 in bf16 (T < 48 on layers of
     8192 outputs or more); above that segment build
-    (unsorted input), the shrink, the v fold (only when the shrink splits d_in)
-    and the tiled GEMM with fused expand; shrink + GEMM for fp32."""
+    (unsorted input), the shrink, the v fold (only when the shrink splits d_in),
+    the dense adapter term (dense_expand) and the tiled GEMM with the term
+    added or expanded in its epilogue; shrink + GEMM for fp32."""
     wide = case.n_tokens >= 48 and case.d_out >= 8192    # api.hip sends these to the GEMM
     if case.dtype == "bf16" and case.n_tokens <= 64 and not wide:
         return ["k_stream_bf16", "k_finish_bf16"]
@@ -230,7 +245,8 @@ def layer_kernels(case):
                  shrink_split(case) == 1 and os.environ.get("MLORA_FORCE_SHRINK") != "mfma")
         return ((["k_build_segments"] if not case.sorted_input else []) +
                 (["k_shrink_short"] if short else ["k_shrink2"]) +
-                (["k_vfinal"] if shrink_split(case) > 1 else []) + ["k_gemm2"])
+                (["k_vfinal"] if shrink_split(case) > 1 else []) +
+                (["k_expand_delta"] if dense_expand(case) else []) + ["k_gemm2"])
     return ["k_shrink_f32", "k_gemm_f32"]
 
 

@@ -64,10 +64,26 @@ bool shape_ok(int d_in, int d_out, int dtype, int max_rank, int capacity) {
 // Workspace layout for up to T tokens.
 struct WsLayout {
   size_t err, token_index, seg_start, seg_adapter, seg_rank, seg_scale, n_seg, counts, v_part,
-      ypart, pos_info, v_fin, total;
+      ypart, pos_info, v_fin, delta, total;
 };
 
 int r_ws_of(int max_rank) { return (max_rank + 15) / 16 * 16; }
+
+// Bytes of the dense adapter term [T][d_out] fp32 of k_expand_delta: bf16
+// pools, up to kDxMaxT tokens and kDxMaxBytes, otherwise none.
+size_t delta_bytes(const mlora_pool_s* p, int T) {
+  if (p->dtype != MLORA_BF16 || T > kDxMaxT) return 0;
+  const size_t b = (size_t)T * p->d_out * 4;
+  return b <= kDxMaxBytes ? b : 0;
+}
+
+// the largest token count up to max_tokens that still has a dense-term region
+int delta_tokens_max(const mlora_pool_s* p, int max_tokens) {
+  if (p->dtype != MLORA_BF16) return 0;
+  const long long by_bytes = (long long)(kDxMaxBytes / ((size_t)p->d_out * 4));
+  long long t = max_tokens < kDxMaxT ? max_tokens : kDxMaxT;
+  return (int)(t < by_bytes ? t : by_bytes);
+}
 
 WsLayout ws_layout(const mlora_pool_s* p, int T) {
   WsLayout L;
@@ -95,6 +111,7 @@ WsLayout ws_layout(const mlora_pool_s* p, int T) {
   L.ypart = take(p->dtype == MLORA_BF16 && T <= 64 ? (size_t)n_chunks * n_tiles * 64 * tt * 4 : 0);
   L.pos_info = take((size_t)T * 16);
   L.v_fin = take((size_t)T * r_ws_of(p->max_rank) * 4);
+  L.delta = take(delta_bytes(p, T));
   L.total = o;
   return L;
 }
@@ -147,6 +164,29 @@ bool debug_validate() {
   return e && e[0] == '1' && e[1] == 0;
 }
 
+// The adapter term as a dense fp32 tile (k_expand_delta, added by the GEMM
+// before its rounding) instead of the GEMM epilogue's MFMA expand: plain bf16
+// pools of rank <= kDxMaxRank with a dense-term region in the workspace, on
+// the tiled GEMM path, for pools whose largest rank is at least 32. The
+// choice depends on the pool and T only, never on the segments, so a batch
+// and its unsorted form (whose segments only the device knows) take the same
+// path and give the same bits. Measured on the heterogeneous batch (256
+// tokens, 5120 -> 5120, 112 adapters of ranks 8-64, mostly one token each):
+// 82.0 us per LoRA-on call against 88.7 with the MFMA expand, whose busiest
+// wave walks 69 (run, 16 rank column) units while others walk 2; on the
+// verify batch (rank 16, two tokens per segment) the MFMA expand stays
+// ahead, 69.7 against 82.9 us. MLORA_EXPAND=dense|mfma forces either where
+// eligible.
+bool use_dense_expand(const mlora_pool_s* p, const SegView& sv, int T, int lora_on) {
+  if (!lora_on || sv.n_seg <= 0 || p->kind == 2 || p->max_rank > kDxMaxRank || p->d_out % 8 != 0 ||
+      delta_bytes(p, T) == 0)
+    return false;
+  const char* e = getenv("MLORA_EXPAND");
+  if (e && !strcmp(e, "dense")) return true;
+  if (e && !strcmp(e, "mfma")) return false;
+  return p->max_rank >= 32;
+}
+
 // Launch the layer on sorted metadata already resident on the device.
 // w_scale != null: W holds FP8 e4m3 codes with a float32 scale per row (bf16
 // pool, split-K decode path only; the caller has checked the shape).
@@ -168,6 +208,7 @@ int run_linear(const void* x, const void* W, mlora_pool_s* pool, const SegView& 
   a.v_fin = (float*)(ws + L.v_fin);
   a.r_ws = r_ws_of(pool->max_rank);
   a.seg_grid = lora_on ? sv.n_seg : 0;
+  a.delta = nullptr;
   if (pool->dtype == MLORA_BF16) {
     const int fp = forced_path();
     // The split-K decode path up to 64 tokens, except on wide layers from 48
@@ -214,8 +255,10 @@ int run_linear(const void* x, const void* W, mlora_pool_s* pool, const SegView& 
       launch_gemv_bf16(a, stream);
       return check_launch();
     }
+    if (use_dense_expand(pool, sv, T, lora_on)) a.delta = (float*)(ws + L.delta);
     if (log_calls())
-      log_call("gemm", T, pool, sv, lora_on, a.ks, !lora_on || a.seg_grid <= 0 ? "none" : shrink_short(a) ? "short" : "mfma");
+      log_call(a.delta ? "gemm-dense-expand" : "gemm", T, pool, sv, lora_on, a.ks,
+               !lora_on || a.seg_grid <= 0 ? "none" : shrink_short(a) ? "short" : "mfma");
     launch_linear_bf16(a, stream);
   } else {
     a.ks = 1;
@@ -425,11 +468,15 @@ int mlora_adapter_rank(mlora_pool_t p, int adapter_id) {
 
 size_t mlora_workspace_bytes(mlora_pool_t p, int max_tokens) {
   if (!p || max_tokens < 0 || max_tokens > MLORA_MAX_TOKENS) return 0;
-  // the layout grows with T within T <= 64 (decode partial tiles) and within
-  // T > 64, but a batch of <= 64 tokens may need more than a larger one
+  // the layout grows with T, except where a region stops: the decode partial
+  // tiles past 64 tokens and the dense adapter term past delta_tokens_max; a
+  // smaller batch may then need more than a larger one, so the size is the
+  // largest of the three candidates
   const size_t big = ws_layout(p, max_tokens).total;
   const size_t small = ws_layout(p, max_tokens < 64 ? max_tokens : 64).total;
-  return big > small ? big : small;
+  const size_t mid = ws_layout(p, delta_tokens_max(p, max_tokens)).total;
+  const size_t m = big > small ? big : small;
+  return m > mid ? m : mid;
 }
 
 int mlora_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream) {

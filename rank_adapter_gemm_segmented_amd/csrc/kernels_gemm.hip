@@ -551,6 +551,83 @@ __global__ __launch_bounds__(256) void k_vfinal(LinearArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Adapter term as a dense fp32 tile, for batches of many short segments of
+// mixed rank: delta[p][n] = sum over j < r of B_a[n][j] * v_fin[p][j] for
+// every sorted position p whose table entry names an adapter, and zero for
+// every other position below T. One workgroup per (position, block of
+// kDxRows rows). L lanes share a row (L = the row's 16-byte chunks, rounded
+// up to a power of two: 1, 2, 4 or 8), lane c taking chunk c (columns
+// 8c .. 8c + 7), so a load instruction covers 64 / L whole B rows of the
+// slot, contiguous; the L partial sums of a row are added in a fixed order
+// (xor partners 1, 2, 4). All of a workgroup's B loads are in flight before
+// its first product. The position's v row, the same for every thread,
+// passes through LDS. Both the padding of B past the rank and v_fin past it
+// are zero, so whole chunks are multiplied. The tiled GEMM adds delta to its
+// accumulators before the single rounding of y.
+// ---------------------------------------------------------------------------
+constexpr int kDxRows = 512;   // rows per workgroup
+
+template <int L>
+__device__ __forceinline__ void expand_rows(const LinearArgs& a, const uint16_t* bslot, int pitch, int n_base,
+                                            f32x4_t vq, bool vt, float* vs, float* __restrict__ drow) {
+  constexpr int RP = 256 / L;                        // rows per pass
+  constexpr int NP = kDxRows / RP;                   // passes
+  const int tid = threadIdx.x, c = tid % L, ro = tid / L;
+  const bool c_ok = 8 * c < pitch;
+  const uint16_t* zeros = (const uint16_t*)a.pv.zeros;
+  u32x4_t b[NP];
+#pragma unroll
+  for (int k = 0; k < NP; ++k) {
+    const int n = n_base + k * RP + ro;
+    // chunks past the row's pitch and rows past d_out read the zero block
+    b[k] = ld16(c_ok && n < a.d_out ? bslot + (long long)n * pitch + 8 * c : zeros);
+  }
+  if (vt) *(f32x4_t*)&vs[4 * tid] = vq;              // waits for the v row alone
+  __syncthreads();
+  const f32x4_t v0 = c_ok ? *(const f32x4_t*)&vs[8 * c] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const f32x4_t v1 = c_ok ? *(const f32x4_t*)&vs[8 * c + 4] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < NP; ++k) {
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t wd = b[k][e / 2];
+      const float bv = __uint_as_float((e & 1) ? (wd & 0xffff0000u) : (wd << 16));
+      s = fmaf(bv, e < 4 ? v0[e] : v1[e - 4], s);
+    }
+    if constexpr (L > 1) s += __shfl_xor(s, 1, L);
+    if constexpr (L > 2) s += __shfl_xor(s, 2, L);
+    if constexpr (L > 4) s += __shfl_xor(s, 4, L);
+    const int n = n_base + k * RP + ro;
+    if (c == 0 && n < a.d_out) drow[n] = s;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_expand_delta(LinearArgs a) {
+  __shared__ __attribute__((aligned(16))) float vs[kDxMaxRank];
+  const int p = blockIdx.y, tid = threadIdx.x;
+  const int n_base = blockIdx.x * kDxRows;
+  float* __restrict__ drow = a.delta + (long long)p * a.d_out;
+  const int4 pi = a.pos_info[p];
+  const bool live = pi.y >= 0 && pi.y < a.pv.capacity && pi.z > 0;
+  if (!live) {                                        // uniform: a zero term
+    for (int n = n_base + tid; n < min(n_base + kDxRows, a.d_out); n += 256) drow[n] = 0.f;
+    return;
+  }
+  const int r = min(min(pi.z, a.pv.max_rank), kDxMaxRank);
+  const int pitch = round_up8(r);
+  const uint16_t* bslot = (const uint16_t*)a.pv.base + (long long)pi.y * a.pv.slot_elems + a.pv.b_offset;
+  // the v row is requested before the B rows and staged in LDS after them
+  // (that store then waits for the v row alone)
+  const bool vt = tid < kDxMaxRank / 4 && 4 * tid < a.r_ws;
+  const f32x4_t vq = *(const f32x4_t*)(vt ? a.v_fin + (long long)p * a.r_ws + 4 * tid : (const float*)a.pv.zeros);
+  if (pitch <= 8) expand_rows<1>(a, bslot, pitch, n_base, vq, vt, vs, drow);
+  else if (pitch <= 16) expand_rows<2>(a, bslot, pitch, n_base, vq, vt, vs, drow);
+  else if (pitch <= 32) expand_rows<4>(a, bslot, pitch, n_base, vq, vt, vs, drow);
+  else expand_rows<8>(a, bslot, pitch, n_base, vq, vt, vs, drow);
+}
+
+// ---------------------------------------------------------------------------
 // GEMM + fused expand
 // ---------------------------------------------------------------------------
 constexpr int kBatch = 8;           // independent loads per thread in bulk LDS copies
@@ -769,8 +846,47 @@ void k_gemm2(LinearArgs a) {
     issue_x(st + NX - 1);
     compute(L + (st % NB) * C::WSTAGE_B, L + C::XRING + (st % NX) * C::XSTAGE_B);
   }
+  // the dense adapter term of k_expand_delta (zero where a position has no
+  // adapter): lane (l32, h) takes rows 8 q + 4 h .. + 3 of each 32-row block
+  // at its position. Small tiles request it here, so it lands while the
+  // ring drains; positions past T and rows past d_out are clamped (neither is
+  // stored).
+  constexpr bool kDeltaEarly = C::MR * C::MT <= 4;
+  const bool use_delta = a.lora_on && a.delta != nullptr;
+  auto delta_ptr = [&](int n, int m, int q) {
+    const int p = min(t0 + wt * WT + n * 32 + l32, T - 1);
+    return a.delta + (long long)p * d_out + min(r0 + wr * WR + m * 32 + 8 * q + 4 * (lane / 32), d_out - 4);
+  };
+  f32x4_t dpre[kDeltaEarly ? C::MT : 1][kDeltaEarly ? C::MR : 1][4];
+  if constexpr (kDeltaEarly) {
+    if (use_delta) {
+#pragma unroll
+      for (int n = 0; n < C::MT; ++n)
+#pragma unroll
+        for (int m = 0; m < C::MR; ++m)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) dpre[n][m][q] = *(const f32x4_t*)delta_ptr(n, m, q);
+    }
+  }
   // the ring's last DMAs (zero stages) land before the LDS is reused
   vm_barrier<0>();
+  if (use_delta) {
+#pragma unroll
+    for (int n = 0; n < C::MT; ++n)
+#pragma unroll
+      for (int m = 0; m < C::MR; ++m) {
+        f32x4_t dv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if constexpr (kDeltaEarly) dv[q] = dpre[n][m][q];
+          else dv[q] = *(const f32x4_t*)delta_ptr(n, m, q);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[m][n][4 * q + i] += dv[q][i];
+      }
+  }
 
   // ---- expand: acc += B_a (scale v) per segment run, on MFMA ---------------
   // scale*v of the tile's positions is staged in LDS (per rank chunk of up to
@@ -779,8 +895,9 @@ void k_gemm2(LinearArgs a) {
   // WT positions on its own, with no block barrier: a work unit is (run,
   // 16 rank columns); the unit's B slice (the wave's WR rows) is loaded from
   // the pool straight into MFMA operand registers, a ring of kEpiRing units
-  // ahead of the unit being multiplied.
-  if (a.lora_on) {
+  // ahead of the unit being multiplied. (With the dense term of
+  // k_expand_delta, added above, none of this runs.)
+  if (a.lora_on && !a.delta) {
     const int RC = a.r_ws < 64 ? a.r_ws : 64;        // rank columns per chunk (16, 32 or 64)
     const int VP = RC + 8;                           // hi/lo row pitch (bf16)
     uint16_t* vsh = lds;
@@ -979,7 +1096,7 @@ void k_gemm2(LinearArgs a) {
   constexpr int YP = WR * 2 + 16;                       // tile row pitch (bytes)
   constexpr int CPR = WR / 8;                           // 16-byte pieces per row
   static_assert(C::NW * WT * YP <= C::LDS_BYTES, "y tile fits the LDS");
-  if (a.lora_on) __syncthreads();                       // the expand's LDS reads are done
+  if (a.lora_on && !a.delta) __syncthreads();          // the expand's LDS reads are done
   char* yt = (char*)lds + wave * WT * YP;
 #pragma unroll
   for (int n = 0; n < C::MT; ++n)
@@ -1115,6 +1232,8 @@ void launch_shrink_bf16(const LinearArgs& a, hipStream_t st) {
 // LoRA-on call dropped from 98 to 88 us.
 void launch_linear_bf16(const LinearArgs& a, hipStream_t st) {
   launch_shrink_bf16(a, st);
+  if (a.lora_on && a.delta && a.seg_grid > 0)
+    hipLaunchKernelGGL(k_expand_delta, dim3((a.d_out + kDxRows - 1) / kDxRows, a.T), dim3(256), 0, st, a);
   auto tiles = [&](int br, int bt) {
     return (long long)((a.d_out + br - 1) / br) * ((a.T + bt - 1) / bt);
   };

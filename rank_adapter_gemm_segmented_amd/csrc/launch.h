@@ -24,10 +24,14 @@ struct LinearArgs {
   int r_ws;        // row pitch of v_part (max_rank rounded up to 16)
   int ks;          // number of d_in chunks of the shrink (1..kMaxShrinkSplit)
   int seg_grid;    // number of segments to cover (upper bound)
+  float* delta;    // workspace: dense adapter term [T][d_out] fp32 (k_expand_delta), or null
 };
 
 constexpr int kMaxShrinkSplit = 16;
 constexpr int kMaxRankWs = 256;   // largest v row pitch (max_rank rounded up to 16)
+constexpr int kDxMaxRank = 64;    // largest rank of the dense-term expand (k_expand_delta)
+constexpr int kDxMaxT = 512;      // most tokens of a call whose workspace holds the dense term
+constexpr size_t kDxMaxBytes = 16u << 20;   // and at most this many bytes of it
 
 // Small-T (decode) path: split-K streaming kernel + finishing kernel.
 constexpr int kDecMaxKc = 1024;   // largest d_in chunk per item

@@ -2,7 +2,8 @@
 summaries) against the kernels the library actually dispatches.
 
 bench.py mirrors the library's host-side choices (decode pair or tiled GEMM,
-which shrink, whether the d_in split needs k_vfinal, device segmentation) in
+which shrink, whether the d_in split needs k_vfinal, device segmentation,
+whether the adapter term is added as a dense tile) in
 Python. With MLORA_LOG=1 the library prints the path, the d_in split and the
 shrink it took; the two must agree on every bench workload, LoRA-on.
 """
@@ -40,8 +41,10 @@ def test_bench_kernel_list_matches_dispatch(name, proj, monkeypatch, capfd):
     expect_path = {"bf16": "gemm", "f32": "f32"}[case.dtype]
     if kernels == ["k_stream_bf16", "k_finish_bf16"]:
         expect_path = "decode"
+    elif "k_expand_delta" in kernels:
+        expect_path = "gemm-dense-expand"
     assert path == expect_path, (path, kernels)
-    if path == "gemm":
+    if path in ("gemm", "gemm-dense-expand"):
         assert ks == bench.shrink_split(case), (ks, bench.shrink_split(case))
         assert ("k_vfinal" in kernels) == (ks > 1)
         assert ("k_shrink_short" in kernels) == (shrink == "short"), (shrink, kernels)
