@@ -1028,12 +1028,17 @@ void k_gemm2(LinearArgs a) {
         const uint16_t* sb = (const uint16_t*)a.pv.base +
                              (live ? (long long)d.z * a.pv.slot_elems + a.pv.b_offset + jc0 + d.y : 0);
         const int col = jc0 + d.y + kh;
+        // columns past the adapter's rank read the zero block: col < rank
+        // implies col + 8 <= the padded row pitch d.w. The address is chosen
+        // with integer masks rather than a pointer select, which the compiler
+        // may turn into divergent branches whose join waits for every load
+        // in flight (the ring would then overlap nothing).
+        const unsigned long long keep = 0ull - (unsigned long long)(live && col < d.w);
 #pragma unroll
         for (int m = 0; m < C::MR; ++m) {
           const int row = min(rowb + m * 32 + l32, d_out - 1);
-          // columns past the adapter's rank read the zero block (no select):
-          // col < rank implies col + 8 <= the padded row pitch d.w
-          ring[slot][m] = ld16(live && col < d.w ? sb + (long long)row * d.w + kh : zeros);
+          const unsigned long long pa = (unsigned long long)(sb + (long long)row * d.w + kh);
+          ring[slot][m] = ld16((const void*)((pa & keep) | ((unsigned long long)zeros & ~keep)));
         }
       };
       // v operands of a unit, one unit ahead (double buffer); the mask of
