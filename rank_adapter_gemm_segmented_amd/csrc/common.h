@@ -45,6 +45,15 @@ __device__ __forceinline__ u32x4_t ld_nt16(const void* p) {
 }
 __device__ __forceinline__ u32x4_t ld16(const void* p) { return *(const u32x4_t*)p; }
 
+// p where cond holds, else alt, chosen with integer masks. A pointer select
+// on a per-lane condition may be compiled into divergent branches, whose
+// join waits for every load in flight; this form stays one vector select.
+// The address not chosen is never dereferenced.
+__device__ __forceinline__ const void* sel_addr(bool cond, const void* p, const void* alt) {
+  const unsigned long long m = 0ull - (unsigned long long)cond;
+  return (const void*)(((unsigned long long)p & m) | ((unsigned long long)alt & ~m));
+}
+
 // Segment containing sorted position p: largest s in [0, n_seg) with
 // seg_start[s] <= p (binary search; seg_start assumed non-decreasing). Returns
 // a value in [0, n_seg-1] for any p, so callers must still check

@@ -226,11 +226,13 @@ __global__ __launch_bounds__(256) void k_shrink2(LinearArgs a) {
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb) prow[rb] = sv.token_index[prow[rb]];
     }
+    bool xok[NRB];
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
       const int p = pg + rb * 16 + l16;
       const int row = min(max(prow[rb], 0), T - 1);
-      xrow[rb] = p < pe ? x + (long long)row * d_in : nullptr;
+      xrow[rb] = x + (long long)row * d_in;
+      xok[rb] = p < pe;
     }
     const int nrb = min(NRB, (pe - pg + 15) / 16);
     for (int jg = jg0; jg < jg1; jg += 16 * NCB) {   // (one pass: the item's rank group)
@@ -245,10 +247,12 @@ __global__ __launch_bounds__(256) void k_shrink2(LinearArgs a) {
         constexpr int DD = 16 / (NRB + NC);
         const int nst_pd = (nst_w + DD - 1) / DD * DD;
         const uint16_t* arow[NC];
+        bool aok[NC];
 #pragma unroll
         for (int cb = 0; cb < NC; ++cb) {
           const int j = jg + cb * 16 + l16;
-          arow[cb] = j < jg1 ? Aa + (long long)j * d_in : nullptr;
+          arow[cb] = Aa + (long long)min(j, jg1 - 1) * d_in;
+          aok[cb] = j < jg1;
         }
         f32x4_t acc[NRB][NC];
 #pragma unroll
@@ -260,9 +264,9 @@ __global__ __launch_bounds__(256) void k_shrink2(LinearArgs a) {
           const int k = (kb + wave + 4 * i) * 32 + kq;
           const bool kin = i < nst && k < d_in;
 #pragma unroll
-          for (int cb = 0; cb < NC; ++cb) af[slot][cb] = ld16(kin && arow[cb] ? arow[cb] + k : zeros + kq);
+          for (int cb = 0; cb < NC; ++cb) af[slot][cb] = ld16(sel_addr(kin && aok[cb], arow[cb] + k, zeros + kq));
 #pragma unroll
-          for (int rb = 0; rb < NRB; ++rb) xf[slot][rb] = ld16(kin && xrow[rb] ? xrow[rb] + k : zeros + kq);
+          for (int rb = 0; rb < NRB; ++rb) xf[slot][rb] = ld16(sel_addr(kin && xok[rb], xrow[rb] + k, zeros + kq));
         };
 #pragma unroll
         for (int u = 0; u < DD; ++u) load(u, u);
@@ -851,7 +855,11 @@ void k_gemm2(LinearArgs a) {
   // at its position. Small tiles request it here, so it lands while the
   // ring drains; positions past T and rows past d_out are clamped (neither is
   // stored).
-  constexpr bool kDeltaEarly = C::MR * C::MT <= 4;
+  // Tiles whose y tile fits the LDS in fp32 add the term while storing y
+  // (kDeltaTile, below), where consecutive lanes read consecutive rows of one
+  // position; the others add it here, from per-lane 16-byte pieces.
+  constexpr bool kDeltaTile = C::NW * WT * (4 * WR + 16) <= C::LDS_BYTES;
+  constexpr bool kDeltaEarly = !kDeltaTile && C::MR * C::MT <= 4;
   const bool use_delta = a.lora_on && a.delta != nullptr;
   auto delta_ptr = [&](int n, int m, int q) {
     const int p = min(t0 + wt * WT + n * 32 + l32, T - 1);
@@ -870,7 +878,7 @@ void k_gemm2(LinearArgs a) {
   }
   // the ring's last DMAs (zero stages) land before the LDS is reused
   vm_barrier<0>();
-  if (use_delta) {
+  if (!kDeltaTile && use_delta) {
 #pragma unroll
     for (int n = 0; n < C::MT; ++n)
 #pragma unroll
@@ -1029,16 +1037,13 @@ void k_gemm2(LinearArgs a) {
                              (live ? (long long)d.z * a.pv.slot_elems + a.pv.b_offset + jc0 + d.y : 0);
         const int col = jc0 + d.y + kh;
         // columns past the adapter's rank read the zero block: col < rank
-        // implies col + 8 <= the padded row pitch d.w. The address is chosen
-        // with integer masks rather than a pointer select, which the compiler
-        // may turn into divergent branches whose join waits for every load
-        // in flight (the ring would then overlap nothing).
-        const unsigned long long keep = 0ull - (unsigned long long)(live && col < d.w);
+        // implies col + 8 <= the padded row pitch d.w. (A pointer select here
+        // compiled into divergent branches whose join waited for every load
+        // in flight: the ring overlapped nothing.)
 #pragma unroll
         for (int m = 0; m < C::MR; ++m) {
           const int row = min(rowb + m * 32 + l32, d_out - 1);
-          const unsigned long long pa = (unsigned long long)(sb + (long long)row * d.w + kh);
-          ring[slot][m] = ld16((const void*)((pa & keep) | ((unsigned long long)zeros & ~keep)));
+          ring[slot][m] = ld16(sel_addr(live && col < d.w, sb + (long long)row * d.w + kh, zeros));
         }
       };
       // v operands of a unit, one unit ahead (double buffer); the mask of
@@ -1102,6 +1107,51 @@ void k_gemm2(LinearArgs a) {
   constexpr int CPR = WR / 8;                           // 16-byte pieces per row
   static_assert(C::NW * WT * YP <= C::LDS_BYTES, "y tile fits the LDS");
   if (a.lora_on && !a.delta) __syncthreads();          // the expand's LDS reads are done
+  uint16_t* __restrict__ y = (uint16_t*)a.y;
+  if constexpr (kDeltaTile) {
+    if (use_delta) {
+      // the tile in fp32 [position][WR]; each lane then takes 8 rows of one
+      // position, adds the dense term's 8 values (one 32-byte run of its row,
+      // consecutive lanes covering the row), rounds once and stores 16 bytes.
+      // The dense term requires d_out % 8 == 0, so every run is whole.
+      constexpr int YP4 = WR * 4 + 16;
+      char* yt4 = (char*)lds + wave * WT * YP4;
+#pragma unroll
+      for (int n = 0; n < C::MT; ++n)
+#pragma unroll
+        for (int m = 0; m < C::MR; ++m)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int rr = m * 32 + 8 * q + 4 * (lane / 32);
+            *(f32x4_t*)(yt4 + (n * 32 + l32) * YP4 + rr * 4) =
+                f32x4_t{acc[m][n][4 * q], acc[m][n][4 * q + 1], acc[m][n][4 * q + 2], acc[m][n][4 * q + 3]};
+          }
+      // (wave-private tile: the wave's own LDS writes are ordered before its reads)
+      const int col = r0 + wr * WR + 8 * (lane % CPR);
+#pragma unroll 2
+      for (int tb = 0; tb < WT; tb += kWave / CPR) {
+        const int tl = tb + lane / CPR;
+        const int p = t0 + wt * WT + tl;
+        if (p >= T || col >= d_out) continue;
+        const float* dsrc = a.delta + (long long)p * d_out + col;
+        const f32x4_t d0 = *(const f32x4_t*)dsrc, d1 = *(const f32x4_t*)(dsrc + 4);
+        int row = a.sv.token_index ? a.sv.token_index[p] : p;
+        row = min(max(row, 0), T - 1);
+        const f32x4_t a0 = *(const f32x4_t*)(yt4 + tl * YP4 + (lane % CPR) * 32);
+        const f32x4_t a1 = *(const f32x4_t*)(yt4 + tl * YP4 + (lane % CPR) * 32 + 16);
+        u32x4_t v;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          v[i] = (uint32_t)f32_to_bf16_bits(a0[2 * i] + d0[2 * i]) |
+                 ((uint32_t)f32_to_bf16_bits(a0[2 * i + 1] + d0[2 * i + 1]) << 16);
+          v[2 + i] = (uint32_t)f32_to_bf16_bits(a1[2 * i] + d1[2 * i]) |
+                     ((uint32_t)f32_to_bf16_bits(a1[2 * i + 1] + d1[2 * i + 1]) << 16);
+        }
+        *(u32x4_t*)(y + (long long)row * d_out + col) = v;
+      }
+      return;
+    }
+  }
   char* yt = (char*)lds + wave * WT * YP;
 #pragma unroll
   for (int n = 0; n < C::MT; ++n)
@@ -1116,7 +1166,6 @@ void k_gemm2(LinearArgs a) {
         *(u32x2_t*)(yt + (n * 32 + l32) * YP + rr * 2) = pk;
       }
   // (wave-private tile: the wave's own LDS writes are ordered before its reads)
-  uint16_t* __restrict__ y = (uint16_t*)a.y;
   const int col = r0 + wr * WR + 8 * (lane % CPR);
   const bool vec = (d_out & 7) == 0 && col + 8 <= d_out;
 #pragma unroll 4
