@@ -3,6 +3,7 @@
 // the entry point that allocates nothing.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -44,10 +45,12 @@ size_t elem_size(int dtype) { return dtype == MLORA_F32 ? 4 : dtype == MLORA_BF1
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-// Slot geometry: A [max_rank, d_in] then B [d_out, round_up8(max_rank)].
-void slot_geometry(int d_in, int d_out, int max_rank, long long* slot_elems, long long* b_off) {
+// Slot geometry: A [max_rank, d_in] then B. bf16 pools store B in blocks of
+// 16 rank columns ([round_up16(max_rank) / 16][d_out][16], see bblk_off);
+// fp32 pools as rows of round_up8(rank) columns ([d_out][round_up8(max_rank)]).
+void slot_geometry(int d_in, int d_out, int max_rank, int dtype, long long* slot_elems, long long* b_off) {
   const long long a_elems = (long long)max_rank * d_in;
-  const long long b_elems = (long long)d_out * ((max_rank + 7) & ~7);
+  const long long b_elems = (long long)d_out * (dtype == MLORA_BF16 ? (max_rank + 15) & ~15 : (max_rank + 7) & ~7);
   *b_off = (a_elems + 127) / 128 * 128;
   *slot_elems = (*b_off + b_elems + 127) / 128 * 128;
 }
@@ -320,7 +323,7 @@ const char* mlora_status_string(int status) {
 size_t mlora_pool_bytes(int d_in, int d_out, int dtype, int max_rank, int capacity) {
   if (!shape_ok(d_in, d_out, dtype, max_rank, capacity)) return 0;
   long long se, bo;
-  slot_geometry(d_in, d_out, max_rank, &se, &bo);
+  slot_geometry(d_in, d_out, max_rank, dtype, &se, &bo);
   const size_t slots = align_up((size_t)capacity * (size_t)se * elem_size(dtype), kAlign);
   return slots + align_up((size_t)capacity * 4, kAlign) + kZeroBytes;
 }
@@ -343,7 +346,7 @@ int mlora_pool_create(void* dev_mem, size_t bytes, int d_in, int d_out, int dtyp
   p->max_rank = max_rank;
   p->capacity = capacity;
   p->elem = elem_size(dtype);
-  slot_geometry(d_in, d_out, max_rank, &p->slot_elems, &p->b_offset);
+  slot_geometry(d_in, d_out, max_rank, dtype, &p->slot_elems, &p->b_offset);
   const size_t slots = align_up((size_t)capacity * (size_t)p->slot_elems * p->elem, kAlign);
   p->dev_rank = (int32_t*)((char*)dev_mem + slots);
   p->zeros = (char*)dev_mem + slots + align_up((size_t)capacity * 4, kAlign);
@@ -364,6 +367,39 @@ int mlora_pool_destroy(mlora_pool_t pool) {
   return MLORA_OK;
 }
 
+// B columns of a slot's region, zero-filled first: bf16 pools hold
+// ceil(rank / 16) blocks of [d_out][16] (bblk_off), fp32 pools d_out rows of
+// round_up8(rank) columns.
+size_t b_region_elems(const mlora_pool_s* p, int rank) {
+  return (size_t)p->d_out * (p->dtype == MLORA_BF16 ? (rank + 15) & ~15 : (rank + 7) & ~7);
+}
+
+// Copy a row-major [rows, r] block of B (source row pitch r) to rows
+// [n_off, n_off + rows) and rank columns [r_off, r_off + r) of the slot's B
+// region (bdst): one 2D copy per block of 16 columns it meets in a bf16
+// pool, one 2D copy of padded rows (pitch bld = round_up8 of the adapter's
+// rank) in an fp32 pool.
+int copy_b(const mlora_pool_s* p, char* bdst, int bld, const void* B, int rows, int n_off, int r_off, int r,
+           hipStream_t stream) {
+  const size_t el = p->elem;
+  if (p->dtype != MLORA_BF16) {
+    const hipError_t e = hipMemcpy2DAsync(bdst + ((size_t)n_off * bld + r_off) * el, (size_t)bld * el, B,
+                                          (size_t)r * el, (size_t)r * el, (size_t)rows, hipMemcpyDefault, stream);
+    return e == hipSuccess ? MLORA_OK : MLORA_ERR_HIP;
+  }
+  for (int c0 = r_off; c0 < r_off + r;) {
+    const int blk = c0 / 16;
+    const int c1 = std::min(r_off + r, 16 * blk + 16);
+    char* dst = bdst + (((size_t)blk * p->d_out + n_off) * 16 + (c0 - 16 * blk)) * el;
+    const char* src = (const char*)B + (size_t)(c0 - r_off) * el;
+    const hipError_t e = hipMemcpy2DAsync(dst, 16 * el, src, (size_t)r * el, (size_t)(c1 - c0) * el, (size_t)rows,
+                                          hipMemcpyDefault, stream);
+    if (e != hipSuccess) return MLORA_ERR_HIP;
+    c0 = c1;
+  }
+  return MLORA_OK;
+}
+
 int mlora_register_adapter(mlora_pool_t p, int adapter_id, int rank, const void* A, const void* B,
                            hipStream_t stream) {
   if (!p || !A || !B) return MLORA_ERR_INVALID_ARG;
@@ -375,17 +411,14 @@ int mlora_register_adapter(mlora_pool_t p, int adapter_id, int rank, const void*
   // A: [rank, d_in] contiguous
   hipError_t e = hipMemcpyAsync(slot, A, (size_t)rank * p->d_in * p->elem, hipMemcpyDefault, stream);
   if (e != hipSuccess) return MLORA_ERR_HIP;
-  // B: [d_out, rank] -> rows padded to round_up8(rank) with zeros
+  // B: [d_out, rank] -> the slot's layout, zero past the rank
   char* bdst = slot + (size_t)p->b_offset * p->elem;
   const int bld = (rank + 7) & ~7;
-  if (bld != rank) {
-    const size_t words = (size_t)p->d_out * bld * p->elem / 4;
-    launch_fill_u32(bdst, words, 0u, stream);
+  if (b_region_elems(p, rank) != (size_t)p->d_out * rank) {
+    launch_fill_u32(bdst, b_region_elems(p, rank) * p->elem / 4, 0u, stream);
     if (check_launch() != MLORA_OK) return MLORA_ERR_HIP;
   }
-  e = hipMemcpy2DAsync(bdst, (size_t)bld * p->elem, B, (size_t)rank * p->elem, (size_t)rank * p->elem,
-                       (size_t)p->d_out, hipMemcpyDefault, stream);
-  if (e != hipSuccess) return MLORA_ERR_HIP;
+  if (copy_b(p, bdst, bld, B, p->d_out, 0, 0, rank, stream) != MLORA_OK) return MLORA_ERR_HIP;
   launch_set_slot_rank(p->dev_rank, adapter_id, rank, stream);
   if (check_launch() != MLORA_OK) return MLORA_ERR_HIP;
   p->host_rank[adapter_id] = rank;
@@ -423,7 +456,7 @@ int mlora_register_adapter_fused(mlora_pool_t p, int adapter_id, int n_slices, c
   char* bdst = slot + (size_t)p->b_offset * p->elem;
   const int bld = (rank + 7) & ~7;
   // B is block-diagonal: zero everywhere, then each slice's block
-  launch_fill_u32(bdst, (size_t)p->d_out * bld * p->elem / 4, 0u, stream);
+  launch_fill_u32(bdst, b_region_elems(p, rank) * p->elem / 4, 0u, stream);
   if (check_launch() != MLORA_OK) return MLORA_ERR_HIP;
   int r_off = 0, n_off = 0;
   for (int m = 0; m < n_slices; ++m) {
@@ -431,10 +464,7 @@ int mlora_register_adapter_fused(mlora_pool_t p, int adapter_id, int n_slices, c
     hipError_t e = hipMemcpyAsync(slot + (size_t)r_off * p->d_in * p->elem, A[m],
                                   (size_t)r * p->d_in * p->elem, hipMemcpyDefault, stream);
     if (e != hipSuccess) return MLORA_ERR_HIP;
-    e = hipMemcpy2DAsync(bdst + ((size_t)n_off * bld + r_off) * p->elem, (size_t)bld * p->elem, B[m],
-                         (size_t)r * p->elem, (size_t)r * p->elem, (size_t)slice_rows[m],
-                         hipMemcpyDefault, stream);
-    if (e != hipSuccess) return MLORA_ERR_HIP;
+    if (copy_b(p, bdst, bld, B[m], slice_rows[m], n_off, r_off, r, stream) != MLORA_OK) return MLORA_ERR_HIP;
     r_off += r;
     n_off += slice_rows[m];
   }

@@ -45,6 +45,15 @@ __device__ __forceinline__ u32x4_t ld_nt16(const void* p) {
 }
 __device__ __forceinline__ u32x4_t ld16(const void* p) { return *(const u32x4_t*)p; }
 
+// Element offset of B[n][j] in a bf16 slot's B region. Rank columns are
+// stored in blocks of 16: block b holds columns 16 b .. 16 b + 15 of every
+// row, [d_out][16] contiguous, so one block's columns over 32 consecutive
+// rows are 1 KB of consecutive bytes (an MFMA operand load of 32 rows then
+// touches 8 cache lines, not one per row). Columns past a rank are zero.
+__device__ __forceinline__ long long bblk_off(int n, int j, int d_out) {
+  return ((long long)(j >> 4) * d_out + n) * 16 + (j & 15);
+}
+
 // p where cond holds, else alt, chosen with integer masks. A pointer select
 // on a per-lane condition may be compiled into divergent branches, whose
 // join waits for every load in flight; this form stays one vector select.

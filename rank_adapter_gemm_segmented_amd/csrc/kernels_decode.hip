@@ -463,7 +463,7 @@ __global__ __launch_bounds__(256) void k_finish_bf16(DecodeArgs a) {
   for (int g = 0; g < kPre; ++g)
 #pragma unroll
     for (int v = 0; v < 4; ++v)
-      b8[g][v] = ld16(Bb + (live ? (long long)min(n + v, d_out - 1) * bld + min(jb + 8 * g, bld - 8) : 0));
+      b8[g][v] = ld16(Bb + (live ? bblk_off(min(n + v, d_out - 1), min(jb + 8 * g, bld - 8), d_out) : 0));
 
   // chunk partials summed in chunk order
   f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -537,7 +537,7 @@ __global__ __launch_bounds__(256) void k_finish_bf16(DecodeArgs a) {
           for (int v = 0; v < 4; ++v) bq[v] = b8[j0 - jb < 8 ? 0 : kPre - 1][v];
         } else {
 #pragma unroll
-          for (int v = 0; v < 4; ++v) bq[v] = ld16(Bb + (long long)min(n + v, d_out - 1) * bld + j0);
+          for (int v = 0; v < 4; ++v) bq[v] = ld16(Bb + bblk_off(min(n + v, d_out - 1), j0, d_out));
         }
 #pragma unroll
         for (int v = 0; v < 4; ++v)
@@ -545,7 +545,7 @@ __global__ __launch_bounds__(256) void k_finish_bf16(DecodeArgs a) {
           for (int e = 0; e < 8; ++e) {
             const uint32_t wd = bq[v][e / 2];
             const float bv = bf16_bits_to_f32((uint16_t)((e & 1) ? (wd >> 16) : (wd & 0xffffu)));
-            // columns j >= r of the padded B row are zero; v there is unused
+            // columns j >= r of B are zero in the pool; v there is unused
             lsum[v] = fmaf(bv, j0 + e < r ? vv[j0 + e] : 0.f, lsum[v]);
           }
       }

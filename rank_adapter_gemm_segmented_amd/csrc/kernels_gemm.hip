@@ -561,8 +561,9 @@ __global__ __launch_bounds__(256) void k_vfinal(LinearArgs a) {
 // every other position below T. One workgroup per (position, block of
 // kDxRows rows). L lanes share a row (L = the row's 16-byte chunks, rounded
 // up to a power of two: 1, 2, 4 or 8), lane c taking chunk c (columns
-// 8c .. 8c + 7), so a load instruction covers 64 / L whole B rows of the
-// slot, contiguous; the L partial sums of a row are added in a fixed order
+// 8c .. 8c + 7), so a load instruction covers 64 / L whole rows, each block
+// of 16 columns contiguous over them; the L partial sums of a row are added
+// in a fixed order
 // (xor partners 1, 2, 4). All of a workgroup's B loads are in flight before
 // its first product. The position's v row, the same for every thread,
 // passes through LDS. Both the padding of B past the rank and v_fin past it
@@ -584,7 +585,7 @@ __device__ __forceinline__ void expand_rows(const LinearArgs& a, const uint16_t*
   for (int k = 0; k < NP; ++k) {
     const int n = n_base + k * RP + ro;
     // chunks past the row's pitch and rows past d_out read the zero block
-    b[k] = ld16(c_ok && n < a.d_out ? bslot + (long long)n * pitch + 8 * c : zeros);
+    b[k] = ld16(c_ok && n < a.d_out ? bslot + bblk_off(n, 8 * c, a.d_out) : zeros);
   }
   if (vt) *(f32x4_t*)&vs[4 * tid] = vq;              // waits for the v row alone
   __syncthreads();
@@ -980,7 +981,7 @@ void k_gemm2(LinearArgs a) {
 
       // unit list of this wave (wave-private LDS), built in parallel: lane l
       // takes run k0 + l and writes one descriptor per 16 rank columns it has
-      // in this chunk: {rs | re << 16, jc, adapter, B row pitch}. A pass
+      // in this chunk: {rs | re << 16, jc, adapter, rank rounded up to 8}. A pass
       // lists at most kEpiMaxUnits units; longer lists take further passes.
       // A fused adapter over stacked projections is nonzero in this wave's
       // rows only in its slice's window of rank columns; units cover that
@@ -1033,17 +1034,18 @@ void k_gemm2(LinearArgs a) {
       const int rowb = r0 + wr * WR;                 // first row of this wave
       auto load_unit = [&](int slot, int4 d, bool ok) {   // d scalar
         const bool live = ok && d.z >= 0;
+        // the unit's 16 columns are one block of B (bblk_off): 32 B per row
         const uint16_t* sb = (const uint16_t*)a.pv.base +
-                             (live ? (long long)d.z * a.pv.slot_elems + a.pv.b_offset + jc0 + d.y : 0);
+                             (live ? (long long)d.z * a.pv.slot_elems + a.pv.b_offset + bblk_off(0, jc0 + d.y, d_out) : 0);
         const int col = jc0 + d.y + kh;
-        // columns past the adapter's rank read the zero block: col < rank
-        // implies col + 8 <= the padded row pitch d.w. (A pointer select here
-        // compiled into divergent branches whose join waited for every load
-        // in flight: the ring overlapped nothing.)
+        // columns past the adapter's rank read the zero block (d.w is the
+        // rank rounded up to 8). (A pointer select here compiled into
+        // divergent branches whose join waited for every load in flight: the
+        // ring overlapped nothing.)
 #pragma unroll
         for (int m = 0; m < C::MR; ++m) {
           const int row = min(rowb + m * 32 + l32, d_out - 1);
-          ring[slot][m] = ld16(sel_addr(live && col < d.w, sb + (long long)row * d.w + kh, zeros));
+          ring[slot][m] = ld16(sel_addr(live && col < d.w, sb + (long long)row * 16 + kh, zeros));
         }
       };
       // v operands of a unit, one unit ahead (double buffer); the mask of

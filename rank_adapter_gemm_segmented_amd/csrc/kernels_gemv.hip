@@ -66,7 +66,6 @@ __global__ __launch_bounds__(kGvThreads) void k_gemv_bf16(LinearArgs a) {
   u32x4_t bq[kGvPre][4];
   f32x4_t vq[kGvPre][2];
   const int ad = pi.y, rk = (ad >= 0 && ad < a.pv.capacity) ? min(pi.z, a.pv.max_rank) : 0;
-  const int pitch = round_up8(rk);
   const uint16_t* brow0 = rk > 0 ? (const uint16_t*)a.pv.base + (long long)ad * a.pv.slot_elems + a.pv.b_offset
                                  : zeros;
   const float* vrow = a.v_fin + (long long)min(p, max(T - 1, 0)) * a.r_ws;
@@ -75,7 +74,7 @@ __global__ __launch_bounds__(kGvThreads) void k_gemv_bf16(LinearArgs a) {
     const bool on = 8 * g < rk;
 #pragma unroll
     for (int v = 0; v < 4; ++v)
-      bq[g][v] = ld16(on ? brow0 + (long long)min(nb + v, d_out - 1) * pitch + 8 * g : zeros);
+      bq[g][v] = ld16(on ? brow0 + bblk_off(min(nb + v, d_out - 1), 8 * g, d_out) : zeros);
     vq[g][0] = on ? *(const f32x4_t*)(vrow + 8 * g) : f32x4_t{0.f, 0.f, 0.f, 0.f};
     vq[g][1] = on ? *(const f32x4_t*)(vrow + 8 * g + 4) : f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
@@ -150,7 +149,7 @@ __global__ __launch_bounds__(kGvThreads) void k_gemv_bf16(LinearArgs a) {
       u32x4_t b[4];
       f32x4_t vv[2];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) b[v] = ld16(brow0 + (long long)min(nb + v, d_out - 1) * pitch + 8 * g);
+      for (int v = 0; v < 4; ++v) b[v] = ld16(brow0 + bblk_off(min(nb + v, d_out - 1), 8 * g, d_out));
       vv[0] = *(const f32x4_t*)(vrow + 8 * g);
       vv[1] = *(const f32x4_t*)(vrow + 8 * g + 4);
       group(b, vv);

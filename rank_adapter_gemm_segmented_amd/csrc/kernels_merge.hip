@@ -17,7 +17,8 @@
 //     reads; a transposed store of 2-byte pieces measured slower, since its
 //     lanes fall on few banks. The B rows of the tile's 64 W rows are loaded
 //     straight into MFMA operand registers (8 consecutive rank entries are
-//     one 16-byte load: pool B rows are zero-padded to a multiple of 8).
+//     one 16-byte load: a bf16 pool stores B in blocks of 16 rank columns,
+//     zero past the rank; an fp32 pool in rows zero-padded to a multiple of 8).
 //     Wave w multiplies columns 32w..32w+31 (MFMA rows) against the tile's
 //     two 32-row blocks (MFMA columns);
 //  3. c * dW (fp32) goes to an LDS tile [64][128]; each thread adds it to its
@@ -105,8 +106,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     for (int s = 0; s < 4; ++s) {
       const int jj = jc + 16 * s + 8 * (lane >> 5);
       const bool on = 16 * s < kr && jj < pitch;
-      bv[s][0] = on ? ld16(B + (long long)nrow0 * pitch + jj) : zero_u32x4();
-      bv[s][1] = on ? ld16(B + (long long)nrow1 * pitch + jj) : zero_u32x4();
+      bv[s][0] = on ? ld16(B + bblk_off(nrow0, jj, d_out)) : zero_u32x4();
+      bv[s][1] = on ? ld16(B + bblk_off(nrow1, jj, d_out)) : zero_u32x4();
     }
     __syncthreads();
     const int mcol = 32 * wave + (lane & 31);  // this lane's MFMA row: a W column of the tile

@@ -61,8 +61,8 @@ struct MergeArgs {
   const void* W_in;
   void* W_out;     // == W_in (in place) or disjoint
   const void* A;   // slot A [rank, d_in]
-  const void* B;   // slot B [d_out, pitch], zero-padded past the rank
-  int d_in, d_out, rank, pitch;
+  const void* B;   // slot B: bf16 blocks of 16 rank columns (bblk_off); fp32 [d_out, pitch]; zero past the rank
+  int d_in, d_out, rank, pitch;   // pitch: the rank rounded up to 8
   float scale;
 };
 

@@ -45,9 +45,12 @@ def test_status_strings():
 
 
 def _geometry(d_in, d_out, elem, max_rank, capacity):
+    # slot: A [max_rank, d_in], then B: bf16 pools in blocks of 16 rank
+    # columns (d_out x max_rank rounded up to 16), fp32 pools in rows of the
+    # rank rounded up to 8
     a = max_rank * d_in
     b_off = (a + 127) // 128 * 128
-    b = d_out * ((max_rank + 7) // 8 * 8)
+    b = d_out * ((max_rank + 15) // 16 * 16 if elem == 2 else (max_rank + 7) // 8 * 8)
     slot = (b_off + b + 127) // 128 * 128
     slots = (capacity * slot * elem + 255) // 256 * 256
     return slots + (capacity * 4 + 255) // 256 * 256 + 4096
