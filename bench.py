@@ -889,10 +889,14 @@ def measure_layer(case, args, label: str):
     """LoRA-on and LoRA-off time of one workload's layer call (ms per call).
 
     Every call takes the next buffer set (W, adapter pool, x, y, workspace)
-    of a rotation covering >= args.rotate_gib GiB, counting on from the
-    warm-up calls, so no timed call reads a set touched fewer than
-    n_sets - 1 calls earlier: the bytes come from HBM, not from the 256 MB
-    Infinity Cache. Returns a dict of times and the set geometry."""
+    of a rotation, counting on from the warm-up calls, so no timed call
+    reads a set touched fewer than n_sets - 1 calls earlier. The rotation is
+    sized by the bytes a LoRA-off call touches (W, x, y), not by whole sets:
+    a set's adapter pool can dwarf its W (671 MB against 52 MB on the
+    heterogeneous batch), and a LoRA-off call never reads it, so sizing by
+    set bytes left that pass's W resident in the 256 MB Infinity Cache. With
+    >= args.rotate_gib GiB of W, x and y in rotation the bytes come from HBM.
+    Returns a dict of times and the set geometry."""
     import numpy as np
     import torch
     import rank_adapter_gemm_segmented_amd as ml
@@ -909,7 +913,8 @@ def measure_layer(case, args, label: str):
         ad = case.adapters[aid]
         pool0.register(aid, to_dev(ad.A, case.dtype), to_dev(ad.B, case.dtype))
     set_bytes = W0.numel() * es + pool0.arena.numel() + x0.numel() * es + T * d_out * es
-    n_sets = 2 if args.profile else max(3, int(np.ceil(args.rotate_gib * (1 << 30) / set_bytes)))
+    touch_bytes = (W0.numel() + x0.numel() + T * d_out) * es
+    n_sets = 2 if args.profile else min(4096, max(3, int(np.ceil(args.rotate_gib * (1 << 30) / touch_bytes))))
     sets = []
     for i in range(n_sets):
         if i == 0:
