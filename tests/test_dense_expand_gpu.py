@@ -29,6 +29,8 @@ SHAPES = [
     (202, 768, 1032, 200, {a: [24, 40, 56, 8, 64][a % 5] for a in range(30)}, False),
     (203, 256, 2048, 512, {a: [64, 32][a % 2] for a in range(90)}, True),
     (204, 1024, 512, 130, {a: [8, 64][a % 2] for a in range(6)}, False),
+    # sorted, mean segment over 16 positions: the shrink's 64-position items
+    (206, 1024, 512, 130, {a: [8, 64][a % 2] for a in range(6)}, True),
 ]
 
 
