@@ -196,11 +196,14 @@ def counted_traffic(workload: str):
 
 def shrink_split(case) -> int:
     """d_in chunks of the bf16 shrink, as the library picks them (api.hip and
-    choose_shrink_split_bf16): one chunk for short segments of rank <= 16, else
-    enough chunks to fill the GPU."""
+    choose_shrink_split_bf16): one chunk for short segments of rank <= 16 and
+    wherever the short-segment shrink runs, else enough chunks to fill the
+    GPU."""
     T = case.n_tokens
     nseg = case.n_seg if case.sorted_input else T   # the host's segment bound
     if T <= 16 * nseg and case.max_rank <= 16:
+        return 1
+    if short_shrink(case):
         return 1
     groups = (case.d_in + 511) // 512
     # items: (block of 16 NRB positions, group of 16 NCB rank rows) per
@@ -212,6 +215,14 @@ def shrink_split(case) -> int:
     while ks < 4 and ks * 2 <= groups and items * ks < 1024:
         ks *= 2
     return ks
+
+
+def short_shrink(case) -> bool:
+    """The vector-ALU shrink for short segments (kernels_gemm.hip,
+    shrink_short): host-known segments, at most two positions per segment on
+    average, ranks <= 32, unless MLORA_FORCE_SHRINK=mfma."""
+    return (case.dtype == "bf16" and case.sorted_input and case.n_tokens <= 2 * case.n_seg and
+            case.max_rank <= 32 and os.environ.get("MLORA_FORCE_SHRINK") != "mfma")
 
 
 def dense_expand(case):
@@ -239,10 +250,8 @@ def layer_kernels(case):
     if case.dtype == "bf16" and case.n_tokens <= 64 and not wide:
         return ["k_stream_bf16", "k_finish_bf16"]
     if case.dtype == "bf16":
-        # the vector-ALU shrink on host-known short segments (kernels_gemm.hip,
-        # shrink_short): at most two positions per segment, ranks <= 16
-        short = (case.sorted_input and case.n_tokens <= 2 * case.n_seg and case.max_rank <= 16 and
-                 shrink_split(case) == 1 and os.environ.get("MLORA_FORCE_SHRINK") != "mfma")
+        # the vector-ALU shrink on host-known short segments
+        short = short_shrink(case)
         return ((["k_build_segments"] if not case.sorted_input else []) +
                 (["k_shrink_short"] if short else ["k_shrink2"]) +
                 (["k_vfinal"] if shrink_split(case) > 1 else []) +

@@ -212,6 +212,7 @@ int run_linear(const void* x, const void* W, mlora_pool_s* pool, const SegView& 
   a.r_ws = r_ws_of(pool->max_rank);
   a.seg_grid = lora_on ? sv.n_seg : 0;
   a.delta = nullptr;
+  a.gorder = 0;
   if (pool->dtype == MLORA_BF16) {
     const int fp = forced_path();
     // The split-K decode path up to 64 tokens, except on wide layers from 48
@@ -248,8 +249,11 @@ int run_linear(const void* x, const void* W, mlora_pool_s* pool, const SegView& 
     }
     // short low-rank segments (a verify batch): one d_in chunk, so the shrink
     // writes the final scaled v and no finalize launch follows (measured
-    // faster there; longer or higher-rank segments gain from the split)
-    const bool one_chunk = lora_on && T <= 16 * a.seg_grid && pool->max_rank <= 16;
+    // faster there; longer or higher-rank segments gain from the split); so
+    // does every batch the short-segment shrink takes (it runs one chunk)
+    LinearArgs one = a;
+    one.ks = 1;
+    const bool one_chunk = lora_on && ((T <= 16 * a.seg_grid && pool->max_rank <= 16) || shrink_short(one));
     a.ks = one_chunk ? 1 : choose_shrink_split_bf16(pool->d_in, shrink_items_bound(T, a.seg_grid, pool->max_rank));
     if (fp == 3 && T <= 64) {
       if (log_calls())

@@ -10,7 +10,7 @@
 //             chunk order and applies the scale (v_fin, read by the epilogue).
 //             With a single chunk the shrink writes v_fin itself.
 //             k_shrink_short replaces it on batches of one- or two-position
-//             segments of rank <= 16 (vector-ALU dot products, real rows only).
+//             segments of rank <= 32 (vector-ALU dot products, real rows only).
 //  k_gemm2    W x as a tiled GEMM on v_mfma_f32_32x32x16_bf16: block tile of
 //             BR W rows x BT sorted positions over the whole of d_in, both
 //             operands staged through LDS by direct-to-LDS loads (a ring of
@@ -339,6 +339,7 @@ __global__ __launch_bounds__(256) void k_shrink2(LinearArgs a) {
 // ---------------------------------------------------------------------------
 constexpr int kSsPos = 4;      // positions per item
 constexpr int kSsRows = 8;     // rank rows per workgroup (4 measured the same, 16 slower)
+constexpr int kSsMaxRank = 32; // largest pool rank it takes
 constexpr int kSsUnroll = 2;   // column groups per thread whose loads are in flight together
 constexpr int kSsPitch = 256 + 8;
 
@@ -737,7 +738,22 @@ void k_gemm2(LinearArgs a) {
   const int l32 = lane % 32, kh = 8 * (lane / 32);
   const int T = a.T, d_in = a.d_in, d_out = a.d_out;
   const int n_rt = (d_out + BR - 1) / BR;
-  const int rt = blockIdx.x % n_rt, tt = blockIdx.x / n_rt;
+  // Block order. One round of blocks (a block per CU or fewer): row tiles
+  // fastest, so the position tiles of one row tile (n_rt apart, on the same
+  // XCD when n_rt % 8 == 0) run together and share that row tile's W in one
+  // L2. More than one round (gorder): block b goes to XCD b % 8, which takes
+  // row tiles xcd, xcd + 8, ... in turn with their position tiles one after
+  // another, so a row tile's W is still read into one L2 once rather than
+  // once per round.
+  int rt, tt;
+  if (a.gorder) {   // uniform; the host sets it only when n_rt % 8 == 0
+    const int j = blockIdx.x >> 3, n_tt = (T + BT - 1) / BT;
+    rt = (j / n_tt) * 8 + (blockIdx.x & 7);
+    tt = j % n_tt;
+  } else {
+    rt = blockIdx.x % n_rt;
+    tt = blockIdx.x / n_rt;
+  }
   const int r0 = rt * BR, t0 = tt * BT;
   const int wr = wave / C::NWT, wt = wave % C::NWT;
   const uint16_t* __restrict__ x = (const uint16_t*)a.x;
@@ -1223,11 +1239,18 @@ int shrink_items_bound(int T, int n_seg_bound, int max_rank) {
   return ((n_seg_bound < kShrMaxSeg ? n_seg_bound : kShrMaxSeg) + (T + pb - 1) / pb) * (ng > 1 ? ng : 1);
 }
 
+// gorder (the XCD-grouped block order of k_gemm2) for launches of more than
+// one block per CU on the HBM-bound tiles: measured on the fused gate|up
+// projection at the verify batch (448 128x128 tiles over 28672 rows), where
+// row tiles fastest left most row tiles' two position tiles in different
+// rounds and read W twice.
 template <int BR, int BT, int WR, int WT, int NB, int KB, int NX>
-static void launch_g(const LinearArgs& a, hipStream_t st) {
+static void launch_g(const LinearArgs& a, hipStream_t st, bool grouped_order) {
   const int n_rt = (a.d_out + BR - 1) / BR, n_tt = (a.T + BT - 1) / BT;
+  LinearArgs g = a;
+  g.gorder = grouped_order && n_tt > 1 && n_rt % 8 == 0 && (long long)n_rt * n_tt > 256;
   hipLaunchKernelGGL((k_gemm2<BR, BT, WR, WT, NB, KB, NX>), dim3(n_rt * n_tt),
-                     dim3(GCfg<BR, BT, WR, WT, NB, KB, NX>::NT), 0, st, a);
+                     dim3(GCfg<BR, BT, WR, WT, NB, KB, NX>::NT), 0, st, g);
 }
 
 // MLORA_FORCE_SHRINK=mfma keeps the MFMA shrink on short segments too.
@@ -1237,13 +1260,16 @@ static bool shrink_short_enabled() {
 }
 
 // The vector-ALU shrink for short segments: a segment count known on the
-// host with at most two positions per segment on average, and ranks up to 16
-// (its items re-read an adapter's A for every kSsPos positions of a longer
-// segment), one d_in chunk. Segments built on the device only bound their
-// count by T, so they keep the MFMA shrink.
+// host with at most two positions per segment on average (its items re-read
+// an adapter's A for every kSsPos positions of a longer segment), ranks up
+// to kSsMaxRank (a workgroup per kSsRows rank rows), one d_in chunk. Segments
+// built on the device only bound their count by T, so they keep the MFMA
+// shrink. Up to rank 32 it covers a fused gate|up pool of two rank-16
+// slices at the verify batch, where the MFMA shrink and its fold took 16.2 +
+// 5.1 us against 9.5 us for one rank-16 projection.
 bool shrink_short(const LinearArgs& a) {
   return a.lora_on && a.ks == 1 && a.sv.n_seg_dev == nullptr && a.seg_grid > 0 && a.T <= 2 * a.seg_grid &&
-         a.pv.max_rank <= 16 && shrink_short_enabled();
+         a.pv.max_rank <= kSsMaxRank && shrink_short_enabled();
 }
 
 void launch_shrink_bf16(const LinearArgs& a, hipStream_t st) {
@@ -1255,7 +1281,7 @@ void launch_shrink_bf16(const LinearArgs& a, hipStream_t st) {
     const dim3 grid(shrink_items_bound(a.T, a.seg_grid, a.pv.max_rank), a.ks);
     const size_t lds = shrink_lds_bytes(a.seg_grid);
     if (shrink_short(a)) {
-      // at most two positions per segment on average, one d_in chunk, ranks <= 16
+      // at most two positions per segment on average, one d_in chunk, ranks <= kSsMaxRank
       const dim3 gs((a.pv.max_rank + kSsRows - 1) / kSsRows, nseg + (a.T + kSsPos - 1) / kSsPos);
       hipLaunchKernelGGL(k_shrink_short, gs, dim3(256), lds, st, a);
       return;
@@ -1294,10 +1320,10 @@ void launch_linear_bf16(const LinearArgs& a, hipStream_t st) {
     return (long long)((a.d_out + br - 1) / br) * ((a.T + bt - 1) / bt);
   };
   constexpr long long kFill = 192;   // tiles that keep most of the 256 CUs busy
-  if (a.T > 128 && tiles(256, 256) >= kFill) launch_g<256, 256, 128, 64, 2, 64, 2>(a, st);
-  else if (a.T > 64 && tiles(128, 128) >= kFill) launch_g<128, 128, 64, 64, 3, 64, 3>(a, st);
-  else if (a.T > 128 && tiles(64, 256) >= kFill) launch_g<64, 256, 64, 64, 3, 64, 3>(a, st);
-  else launch_g<64, 128, 64, 32, 4, 64, 4>(a, st);
+  if (a.T > 128 && tiles(256, 256) >= kFill) launch_g<256, 256, 128, 64, 2, 64, 2>(a, st, false);
+  else if (a.T > 64 && tiles(128, 128) >= kFill) launch_g<128, 128, 64, 64, 3, 64, 3>(a, st, true);
+  else if (a.T > 128 && tiles(64, 256) >= kFill) launch_g<64, 256, 64, 64, 3, 64, 3>(a, st, true);
+  else launch_g<64, 128, 64, 32, 4, 64, 4>(a, st, true);
 }
 
 }  // namespace mlora

@@ -25,6 +25,8 @@ struct LinearArgs {
   int ks;          // number of d_in chunks of the shrink (1..kMaxShrinkSplit)
   int seg_grid;    // number of segments to cover (upper bound)
   float* delta;    // workspace: dense adapter term [T][d_out] fp32 (k_expand_delta), or null
+  int gorder;      // tiled GEMM block order (set by its launcher): 0 row tiles fastest,
+                   // 1 XCD-grouped (row tiles per XCD, their position tiles adjacent)
 };
 
 constexpr int kMaxShrinkSplit = 16;
