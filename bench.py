@@ -254,7 +254,7 @@ def layer_kernels(case):
         short = short_shrink(case)
         return ((["k_build_segments"] if not case.sorted_input else []) +
                 (["k_shrink_short"] if short else ["k_shrink2"]) +
-                (["k_vfinal"] if shrink_split(case) > 1 else []) +
+                (["k_vfinal"] if shrink_split(case) > 1 and not dense_expand(case) else []) +
                 (["k_expand_delta"] if dense_expand(case) else []) + ["k_gemm2"])
     return ["k_shrink_f32", "k_gemm_f32"]
 

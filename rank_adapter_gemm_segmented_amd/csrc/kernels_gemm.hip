@@ -624,9 +624,30 @@ __global__ __launch_bounds__(256) void k_expand_delta(LinearArgs a) {
   const int pitch = round_up8(r);
   const uint16_t* bslot = (const uint16_t*)a.pv.base + (long long)pi.y * a.pv.slot_elems + a.pv.b_offset;
   // the v row is requested before the B rows and staged in LDS after them
-  // (that store then waits for the v row alone)
+  // (that store then waits for the v row alone). With a d_in split of the
+  // shrink (ks > 1) no k_vfinal runs: the row is the chunk partials summed in
+  // chunk order and scaled, zero past the rank, as k_vfinal would write it.
   const bool vt = tid < kDxMaxRank / 4 && 4 * tid < a.r_ws;
-  const f32x4_t vq = *(const f32x4_t*)(vt ? a.v_fin + (long long)p * a.r_ws + 4 * tid : (const float*)a.pv.zeros);
+  f32x4_t vq;
+  if (a.ks > 1) {   // uniform
+    f32x4_t part[kShrMaxSplit];
+#pragma unroll
+    for (int c = 0; c < kShrMaxSplit; ++c)
+      part[c] = *(const f32x4_t*)(vt ? a.v_part + ((long long)min(c, a.ks - 1) * a.T + p) * a.r_ws + 4 * tid
+                                     : (const float*)a.pv.zeros);
+    vq = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < kShrMaxSplit; ++c)
+      if (c < a.ks) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vq[i] += part[c][i];
+      }
+    const float sc = __int_as_float(pi.w);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vq[i] = 4 * tid + i < r ? vq[i] * sc : 0.f;
+  } else {
+    vq = *(const f32x4_t*)(vt ? a.v_fin + (long long)p * a.r_ws + 4 * tid : (const float*)a.pv.zeros);
+  }
   if (pitch <= 8) expand_rows<1>(a, bslot, pitch, n_base, vq, vt, vs, drow);
   else if (pitch <= 16) expand_rows<2>(a, bslot, pitch, n_base, vq, vt, vs, drow);
   else if (pitch <= 32) expand_rows<4>(a, bslot, pitch, n_base, vq, vt, vs, drow);
@@ -1288,7 +1309,7 @@ void launch_shrink_bf16(const LinearArgs& a, hipStream_t st) {
     }
     if (long_segs) hipLaunchKernelGGL((k_shrink2<4, 4>), grid, dim3(256), lds, st, a);
     else hipLaunchKernelGGL((k_shrink2<1, 1>), grid, dim3(256), lds, st, a);
-    if (a.ks > 1) {
+    if (a.ks > 1 && !a.delta) {   // (the dense term's expand folds the chunks itself)
       const int n4 = a.T * (a.r_ws / 4);
       hipLaunchKernelGGL(k_vfinal, dim3((n4 + 255) / 256), dim3(256), 0, st, a);
     }
