@@ -218,10 +218,11 @@ int run_linear(const void* x, const void* W, mlora_pool_s* pool, const SegView& 
     // The split-K decode path up to 64 tokens, except on wide layers from 48
     // tokens up; the tiled GEMM otherwise. Measured per path, token count and
     // pass with HBM counters in profiles/path_sweep.txt: on 4096 -> 4096 the
-    // decode pair is the fastest LoRA-on path at 1-64 tokens (14.6-17.6 us,
-    // GEMM 39-48 us); on 4096 -> 14336 the GEMM wins from 48 tokens (48.2 vs
-    // 51.7 us LoRA-on, 31.8 vs 43.6 us LoRA-off). Both passes of a shape and
-    // token count take the same path, so a zero B reproduces the LoRA-off bits.
+    // decode pair is the fastest LoRA-on path at every count from 1 to 64
+    // (the GEMM takes 2-3x as long there); on 4096 -> 14336 the GEMM is
+    // faster in both passes from 48 tokens and the decode pair below. Both
+    // passes of a shape and token count take the same path, so a zero B
+    // reproduces the LoRA-off bits.
     const bool wide = T >= 48 && pool->d_out >= 8192;
     const bool dec_ok = decode_supported(T, lora_on ? sv.n_seg : 0, pool->d_out, pool->max_rank);
     if (w_scale || (dec_ok && (fp == 1 || (fp == 0 && !wide)))) {

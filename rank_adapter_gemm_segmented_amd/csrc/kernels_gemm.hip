@@ -1332,7 +1332,13 @@ void launch_shrink_bf16(const LinearArgs& a, hipStream_t st) {
 // W rings gained nothing there), its waves split by positions (64 rows x 32
 // positions each): a wave then walks the segment runs of 32 positions, not
 // 64, in units of 2 KB of B rather than 1 KB, and the heterogeneous batch's
-// LoRA-on call dropped from 98 to 88 us.
+// LoRA-on call dropped from 98 to 88 us. Later, with rotations sized by W,
+// x and y: the 128x128 and 64x128 tiles in 8 waves (two per SIMD; waves of
+// 64x32 and 32x32) beat their 4-wave forms on the verify batch (67.0-67.4
+// against 70.6-71.3 us LoRA-on, 47.3 against 48.2-49.0 us off) and the
+// heterogeneous one (82.6-82.9 against 84.7 us, 39.2 against 40.5 us): each
+// CU then keeps twice the waves issuing loads; deeper rings or 2x2-wave
+// shapes did not do better.
 void launch_linear_bf16(const LinearArgs& a, hipStream_t st) {
   launch_shrink_bf16(a, st);
   if (a.lora_on && a.delta && a.seg_grid > 0)
@@ -1342,9 +1348,9 @@ void launch_linear_bf16(const LinearArgs& a, hipStream_t st) {
   };
   constexpr long long kFill = 192;   // tiles that keep most of the 256 CUs busy
   if (a.T > 128 && tiles(256, 256) >= kFill) launch_g<256, 256, 128, 64, 2, 64, 2>(a, st, false);
-  else if (a.T > 64 && tiles(128, 128) >= kFill) launch_g<128, 128, 64, 64, 3, 64, 3>(a, st, true);
+  else if (a.T > 64 && tiles(128, 128) >= kFill) launch_g<128, 128, 64, 32, 3, 64, 3>(a, st, true);
   else if (a.T > 128 && tiles(64, 256) >= kFill) launch_g<64, 256, 64, 64, 3, 64, 3>(a, st, true);
-  else launch_g<64, 128, 64, 32, 4, 64, 4>(a, st, true);
+  else launch_g<64, 128, 32, 32, 4, 64, 4>(a, st, true);
 }
 
 }  // namespace mlora
