@@ -290,7 +290,8 @@ __global__ __launch_bounds__(kDecThreads) void k_stream_bf16(DecodeArgs a) {
       f32x4_t o;
 #pragma unroll
       for (int v = 0; v < 4; ++v) o[v] = acc[tb][v] + sm.red[rb][lane][tb * 4 + v];
-      *(f32x4_t*)(a.ypart + part_off(c, tile, rb, tb, a.n_tiles, NTB) + lane * 4) = o;
+      // (nontemporal: the finish kernel reads it once, from another XCD)
+      __builtin_nontemporal_store(o, (f32x4_t*)(a.ypart + part_off(c, tile, rb, tb, a.n_tiles, NTB) + lane * 4));
     }
   }
 
@@ -340,7 +341,7 @@ __global__ __launch_bounds__(kDecThreads) void k_stream_bf16(DecodeArgs a) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int jr = 4 * (lane / 16) + v;
-        if (jr < rows && t >= ps && t < pe) vp[(long long)t * a.r_ws + j0 + jr] = vacc[tb][v];
+        if (jr < rows && t >= ps && t < pe) __builtin_nontemporal_store(vacc[tb][v], vp + (long long)t * a.r_ws + j0 + jr);
       }
     }
     bi = ni;
@@ -383,12 +384,15 @@ __global__ __launch_bounds__(256) void k_finish_bf16(DecodeArgs a) {
   int row = a.sv.token_index ? a.sv.token_index[tc] : tc;
   const int4 pe = lora ? a.pos[tc] : make_int4(-1, 0, 0, 0);
 
-  // the chunk partials, all loads in flight
+  // the chunk partials, all loads in flight (nontemporal, as they were
+  // written: each is read once; measured 0.6 us faster per LoRA-on call on
+  // the decode batch, same bits)
   const float* pbase = a.ypart + part_off(0, tile, rb, tb, a.n_tiles, NTB) + lane * 4;
   const long long cstride = (long long)a.n_tiles * 4 * NTB * 256;
   f32x4_t p[kFinUnroll];
 #pragma unroll
-  for (int u = 0; u < kFinUnroll; ++u) p[u] = *(const f32x4_t*)(pbase + min(u, a.n_chunks - 1) * cstride);
+  for (int u = 0; u < kFinUnroll; ++u)
+    p[u] = __builtin_nontemporal_load((const f32x4_t*)(pbase + min(u, a.n_chunks - 1) * cstride));
   // FP8 weight: the row scales of the lane's 4 rows
   float wsc[4] = {1.f, 1.f, 1.f, 1.f};
   if constexpr (W8) {
@@ -477,7 +481,8 @@ __global__ __launch_bounds__(256) void k_finish_bf16(DecodeArgs a) {
     }
   for (int c0 = kFinUnroll; c0 < a.n_chunks; c0 += kFinUnroll) {
 #pragma unroll
-    for (int u = 0; u < kFinUnroll; ++u) p[u] = *(const f32x4_t*)(pbase + min(c0 + u, a.n_chunks - 1) * cstride);
+    for (int u = 0; u < kFinUnroll; ++u)
+      p[u] = __builtin_nontemporal_load((const f32x4_t*)(pbase + min(c0 + u, a.n_chunks - 1) * cstride));
 #pragma unroll
     for (int u = 0; u < kFinUnroll; ++u)
       if (c0 + u < a.n_chunks) {
