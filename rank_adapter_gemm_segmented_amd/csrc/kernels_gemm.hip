@@ -679,6 +679,16 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t m0) {
 
 // Wait until at most N of this wave's vector memory operations are in flight,
 // then a workgroup barrier (LDS and scalar counters drained too; nothing else).
+// The same load marked nontemporal, for the W rows (each read once): measured
+// on the verify and heterogeneous batches, their LoRA-off passes took 1-2 us
+// less (45.2-46.3 against 47.3-47.8 us, 38.0 against 39.1 us) with the
+// positions' loads left as they are (those rows are re-read by every row
+// tile and lost 5-18% marked nontemporal).
+__device__ __forceinline__ void dma16_nt(const void* g, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(g), "s"(m0)
+               : "memory", "m0");
+}
+
 template <int N>
 __device__ __forceinline__ void vm_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
@@ -808,15 +818,22 @@ void k_gemm2(LinearArgs a) {
   // W rows of stage st -> W slot st % NB, positions -> position slot
   // st % NX; stages past d_in (and the k tail) read the zero block, so every
   // stage issues the same DMA count and the rings' vmcnt waits stay exact
+  // (W rows: i0 == 0, nontemporal; positions: i0 == DPW_W)
   auto issue_part = [&](int st, int i0, int n, uint32_t sb) {
     const int k0 = st * KB;
     if (k0 + KB <= d_in) {   // uniform: whole stage inside d_in
 #pragma unroll
-      for (int i = 0; i < n; ++i) dma16(src[i0 + i] + k0, sb + (uint32_t)i * C::NW * 1024);
+      for (int i = 0; i < n; ++i) {
+        if (i0 == 0) dma16_nt(src[i0 + i] + k0, sb + (uint32_t)i * C::NW * 1024);
+        else dma16(src[i0 + i] + k0, sb + (uint32_t)i * C::NW * 1024);
+      }
     } else {
 #pragma unroll
-      for (int i = 0; i < n; ++i)
-        dma16(k0 + scol[i0 + i] < d_in ? src[i0 + i] + k0 : zeros, sb + (uint32_t)i * C::NW * 1024);
+      for (int i = 0; i < n; ++i) {
+        const void* g = k0 + scol[i0 + i] < d_in ? src[i0 + i] + k0 : zeros;
+        if (i0 == 0) dma16_nt(g, sb + (uint32_t)i * C::NW * 1024);
+        else dma16(g, sb + (uint32_t)i * C::NW * 1024);
+      }
     }
   };
   auto issue_w = [&](int st) {
