@@ -213,6 +213,7 @@ int run_linear(const void* x, const void* W, mlora_pool_s* pool, const SegView& 
   a.seg_grid = lora_on ? sv.n_seg : 0;
   a.delta = nullptr;
   a.gorder = 0;
+  a.wnt = 0;
   if (pool->dtype == MLORA_BF16) {
     const int fp = forced_path();
     // The split-K decode path up to 64 tokens, except on wide layers from 48

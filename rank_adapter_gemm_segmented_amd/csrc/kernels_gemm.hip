@@ -679,11 +679,12 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t m0) {
 
 // Wait until at most N of this wave's vector memory operations are in flight,
 // then a workgroup barrier (LDS and scalar counters drained too; nothing else).
-// The same load marked nontemporal, for the W rows (each read once): measured
-// on the verify and heterogeneous batches, their LoRA-off passes took 1-2 us
-// less (45.2-46.3 against 47.3-47.8 us, 38.0 against 39.1 us) with the
-// positions' loads left as they are (those rows are re-read by every row
-// tile and lost 5-18% marked nontemporal).
+// The same load marked nontemporal, for W rows that the launch reads once
+// (at most two position tiles, which run in the same round): measured on the
+// verify and heterogeneous batches, their LoRA-off passes took 1-2 us less
+// (45.2-46.3 against 47.3-47.8 us, 38.0 against 39.1 us). Where more position
+// tiles re-read a W panel in later rounds (prefill) the mark lost about 10%
+// (gate/up), and the positions' rows, re-read by every row tile, lost 5-18%.
 __device__ __forceinline__ void dma16_nt(const void* g, uint32_t m0) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(g), "s"(m0)
                : "memory", "m0");
@@ -818,20 +819,21 @@ void k_gemm2(LinearArgs a) {
   // W rows of stage st -> W slot st % NB, positions -> position slot
   // st % NX; stages past d_in (and the k tail) read the zero block, so every
   // stage issues the same DMA count and the rings' vmcnt waits stay exact
-  // (W rows: i0 == 0, nontemporal; positions: i0 == DPW_W)
+  // (W rows: i0 == 0, nontemporal when a.wnt; positions: i0 == DPW_W)
+  const bool wnt = a.wnt != 0;
   auto issue_part = [&](int st, int i0, int n, uint32_t sb) {
     const int k0 = st * KB;
     if (k0 + KB <= d_in) {   // uniform: whole stage inside d_in
 #pragma unroll
       for (int i = 0; i < n; ++i) {
-        if (i0 == 0) dma16_nt(src[i0 + i] + k0, sb + (uint32_t)i * C::NW * 1024);
+        if (i0 == 0 && wnt) dma16_nt(src[i0 + i] + k0, sb + (uint32_t)i * C::NW * 1024);
         else dma16(src[i0 + i] + k0, sb + (uint32_t)i * C::NW * 1024);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < n; ++i) {
         const void* g = k0 + scol[i0 + i] < d_in ? src[i0 + i] + k0 : zeros;
-        if (i0 == 0) dma16_nt(g, sb + (uint32_t)i * C::NW * 1024);
+        if (i0 == 0 && wnt) dma16_nt(g, sb + (uint32_t)i * C::NW * 1024);
         else dma16(g, sb + (uint32_t)i * C::NW * 1024);
       }
     }
@@ -1287,6 +1289,7 @@ static void launch_g(const LinearArgs& a, hipStream_t st, bool grouped_order) {
   const int n_rt = (a.d_out + BR - 1) / BR, n_tt = (a.T + BT - 1) / BT;
   LinearArgs g = a;
   g.gorder = grouped_order && n_tt > 1 && n_rt % 8 == 0 && (long long)n_rt * n_tt > 256;
+  g.wnt = n_tt <= 2;
   hipLaunchKernelGGL((k_gemm2<BR, BT, WR, WT, NB, KB, NX>), dim3(n_rt * n_tt),
                      dim3(GCfg<BR, BT, WR, WT, NB, KB, NX>::NT), 0, st, g);
 }

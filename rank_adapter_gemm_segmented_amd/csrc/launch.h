@@ -27,6 +27,7 @@ struct LinearArgs {
   float* delta;    // workspace: dense adapter term [T][d_out] fp32 (k_expand_delta), or null
   int gorder;      // tiled GEMM block order (set by its launcher): 0 row tiles fastest,
                    // 1 XCD-grouped (row tiles per XCD, their position tiles adjacent)
+  int wnt;         // tiled GEMM: stage W rows by nontemporal loads (set by its launcher)
 };
 
 constexpr int kMaxShrinkSplit = 16;
