@@ -1101,7 +1101,9 @@ void k_gemm2(LinearArgs a) {
 #pragma unroll
         for (int m = 0; m < C::MR; ++m) {
           const int row = min(rowb + m * 32 + l32, d_out - 1);
-          ring[slot][m] = ld16(sel_addr(live && col < d.w, sb + (long long)row * 16 + kh, zeros));
+          // (nontemporal: a unit's B rows are read by this workgroup alone;
+          // the verify pass's LoRA-on call took 3 us less, same bits)
+          ring[slot][m] = ld_nt16(sel_addr(live && col < d.w, sb + (long long)row * 16 + kh, zeros));
         }
       };
       // v operands of a unit, one unit ahead (double buffer); the mask of
