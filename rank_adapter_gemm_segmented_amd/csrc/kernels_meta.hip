@@ -53,23 +53,38 @@ void launch_token_map(const int32_t* seg_start, const int32_t* seg_adapter, int 
 // LDS (one wave-level scan, one cross-wave step). The rank and scale loads stay
 // in flight through the stable count (its barrier waits for LDS only) and land
 // in LDS just before the segment phase, which is their first use.
+//
+// The count is O(T^2) compares, so it is laid out for the vector ALUs: a wave
+// takes 64 consecutive tokens (one per lane) against a range of the other
+// tokens u, read as 4 ids per 16-byte LDS read at a wave-uniform address
+// (a broadcast). Every u below the wave's 64 tokens precedes each of them, so
+// it counts when id[u] <= id[t]; every u above them counts when id[u] < id[t];
+// only the 64 u of the wave's own tokens need the full test. With few tokens
+// the u range is split over several waves whose counts are added in LDS.
 // ---------------------------------------------------------------------------
 constexpr int kSegThreads = 1024;
+constexpr int kSegWaves = kSegThreads / kWave;
 constexpr int kSegPerThread = MLORA_MAX_UNSORTED_TOKENS / kSegThreads;   // tokens per thread (8)
+
+__device__ __forceinline__ int count_le4(int4 o, int k) { return (o.x <= k) + (o.y <= k) + (o.z <= k) + (o.w <= k); }
+__device__ __forceinline__ int count_lt4(int4 o, int k) { return (o.x < k) + (o.y < k) + (o.z < k) + (o.w < k); }
 
 __global__ __launch_bounds__(kSegThreads) void k_build_segments(
     const int32_t* __restrict__ token_adapter, const float* __restrict__ adapter_scale, int T,
     PoolView pv, int32_t* __restrict__ token_index, int32_t* __restrict__ seg_start,
     int32_t* __restrict__ seg_adapter, int32_t* __restrict__ seg_rank,
     float* __restrict__ seg_scale, int32_t* __restrict__ n_seg_out) {
-  // LDS: ids [T] (batch order), srt [T] (sorted position -> batch row),
-  // trk [T] and tsc [T] (registered rank and scale of each batch row's adapter)
-  extern __shared__ int32_t sm[];
+  // LDS: ids [Tp] (batch order, padded to a multiple of 4 with INT_MAX, which
+  // no count includes), srt [T] (sorted position -> batch row), trk [T] and
+  // tsc [T] (registered rank and scale of each batch row's adapter)
+  extern __shared__ __attribute__((aligned(16))) int32_t sm[];
+  const int Tp = (T + 3) & ~3;
   int32_t* ids = sm;
-  int32_t* srt = sm + T;
-  int32_t* trk = sm + 2 * T;
-  float* tsc = (float*)(sm + 3 * T);
-  __shared__ int wtot[kSegThreads / kWave];
+  int32_t* srt = sm + Tp;
+  int32_t* trk = sm + Tp + T;
+  float* tsc = (float*)(sm + Tp + 2 * T);
+  __shared__ int wtot[kSegWaves];
+  __shared__ int part[kSegThreads];   // per-range counts when the u range is split
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
 
   // ---- ids, ranks, scales: token t = tid + kSegThreads * i -----------------
@@ -89,24 +104,48 @@ __global__ __launch_bounds__(kSegThreads) void k_build_segments(
     sc[i] = valid ? adapter_scale[key[i]] : 0.0f;
     if (t < T) ids[t] = key[i];
   }
+  if (tid < Tp - T) ids[T + tid] = 0x7fffffff;
   lds_barrier();
 
-  // ---- stable rank of every token: G threads share one token's count -------
-  int G = 1;
-  while (G < kWave && T * G * 2 <= kSegThreads) G *= 2;
-  for (int t0 = 0; t0 < T; t0 += kSegThreads / G) {   // uniform
-    const int t = t0 + tid / G, sub = tid % G;
+  // ---- stable rank of every token ------------------------------------------
+  // task q (wave-uniform): token group q % ntg (64 tokens), u range q / ntg of G
+  const int ntg = (T + kWave - 1) / kWave;
+  const int G = ntg >= kSegWaves ? 1 : kSegWaves / max(ntg, 1);
+  const int q4 = Tp / 4;
+  for (int q = wave; q < ntg * G; q += kSegWaves) {
+    const int tg = q % ntg, g = q / ntg;
+    const int t = tg * kWave + lane;
     const int k = t < T ? ids[t] : 0;
+    const int ua = 4 * (int)((long long)q4 * g / G), ub = 4 * (int)((long long)q4 * (g + 1) / G);
+    const int lo = tg * kWave, hi = min(lo + kWave, Tp);
     int pos = 0;
-    if (t < T)
-      for (int u = sub; u < T; u += G) {
-        const int o = ids[u];
-        pos += (o < k) | ((o == k) & (u < t));
+    for (int u = ua; u < min(ub, lo); u += 4) pos += count_le4(*(const int4*)&ids[u], k);
+    for (int u = max(ua, lo); u < min(ub, hi); u += 4) {
+      const int4 o = *(const int4*)&ids[u];
+      // lane j's own token is u = lo + j: tokens of lower lanes precede it
+      const int j = u - lo;
+      pos += lane > j + 0 ? (o.x <= k) : (o.x < k);
+      pos += lane > j + 1 ? (o.y <= k) : (o.y < k);
+      pos += lane > j + 2 ? (o.z <= k) : (o.z < k);
+      pos += lane > j + 3 ? (o.w <= k) : (o.w < k);
+    }
+    for (int u = max(ua, hi); u < ub; u += 4) pos += count_lt4(*(const int4*)&ids[u], k);
+    if (G == 1) {
+      if (t < T) {
+        srt[pos] = t;
+        token_index[pos] = t;
       }
-    for (int off = 1; off < G; off <<= 1) pos += __shfl_xor(pos, off, kWave);
-    if (t < T && sub == 0) {
-      srt[pos] = t;
-      token_index[pos] = t;
+    } else {
+      part[g * ntg * kWave + t] = pos;   // G * ntg <= kSegWaves: within part
+    }
+  }
+  if (G > 1) {   // uniform
+    lds_barrier();
+    if (tid < T) {   // T <= ntg * 64 <= kSegThreads / 2 here
+      int pos = 0;
+      for (int g = 0; g < G; ++g) pos += part[g * ntg * kWave + tid];
+      srt[pos] = tid;
+      token_index[pos] = tid;
     }
   }
 #pragma unroll
@@ -151,7 +190,7 @@ __global__ __launch_bounds__(kSegThreads) void k_build_segments(
   }
 }
 
-size_t build_segments_lds_bytes(int T) { return (size_t)4 * T * sizeof(int32_t); }
+size_t build_segments_lds_bytes(int T) { return (size_t)(((T + 3) & ~3) + 3 * T) * sizeof(int32_t); }
 
 void launch_build_segments(const int32_t* token_adapter, const float* adapter_scale, int T,
                            const PoolView& pv, int32_t* token_index, int32_t* seg_start,

@@ -181,6 +181,43 @@ def test_build_segments_at_the_token_limit():
     assert np.array_equal(sr[:S].cpu().numpy(), np.array([c.adapters[a].rank if a >= 0 else 0 for a in o_sa]))
 
 
+@pytest.mark.parametrize("T", [1, 3, 64, 65, 130, 256, 511, 513, 1024, 1100, 3000])
+def test_build_segments_stable_grouping(T):
+    # Canonical segmentation is a stable sort of the rows by id: ids ascending,
+    # rows of one id in batch order, one segment per distinct id. Ids outside
+    # [-1, capacity) (down to INT32_MIN, up to INT32_MAX) stay segments of
+    # their own value with rank 0 and scale 0. Sizes span one to several
+    # 64-token groups, split and unsplit count ranges, and ragged tails.
+    ml = _ml()
+    log(f"[parity] build_segments stable grouping T={T}")
+    rng = np.random.default_rng(900 + T)
+    cap = 40
+    extreme = np.array([-2**31, -7, -2, cap, 99999, 2**31 - 2, 2**31 - 1], np.int64)
+    ids = np.where(rng.random(T) < 0.15, rng.choice(extreme, size=T),
+                   rng.integers(-1, cap, size=T)).astype(np.int32)
+    pool = ml.Pool(64, 64, torch.bfloat16, 16, cap)
+    ranks = {a: [8, 16][a % 2] for a in range(0, cap, 3)}
+    for a, r in ranks.items():
+        pool.register(a, torch.zeros(r, 64, dtype=torch.bfloat16, device="cuda"),
+                      torch.zeros(64, r, dtype=torch.bfloat16, device="cuda"))
+    scale = (np.arange(cap, dtype=np.float32) + 1) / 8
+    ti, ss, sa, sr, sc, ns = ml.build_segments(i32(ids), f32(scale), pool)
+    torch.cuda.synchronize()
+    order = np.argsort(ids, kind="stable")
+    sid = ids[order]
+    starts = np.flatnonzero(np.r_[True, sid[1:] != sid[:-1]])
+    S = int(ns.item())
+    assert S == len(starts)
+    assert np.array_equal(ti.cpu().numpy(), order)
+    assert np.array_equal(ss[:S + 1].cpu().numpy(), np.r_[starts, T])
+    assert np.array_equal(sa[:S].cpu().numpy(), sid[starts])
+    valid = [0 <= a < cap for a in sid[starts]]
+    assert np.array_equal(sr[:S].cpu().numpy(),
+                          [ranks.get(int(a), 0) if v else 0 for a, v in zip(sid[starts], valid)])
+    assert np.array_equal(sc[:S].cpu().numpy(),
+                          np.array([scale[a] if v else 0 for a, v in zip(sid[starts], valid)], np.float32))
+
+
 def test_debug_validate_mode(monkeypatch):
     # MLORA_DEBUG_VALIDATE=1: bad metadata is reported by the layer call itself
     # (and nothing is written); good metadata gives the ordinary result
