@@ -26,7 +26,8 @@ struct LinearArgs {
   int seg_grid;    // number of segments to cover (upper bound)
   float* delta;    // workspace: dense adapter term [T][d_out] fp32 (k_expand_delta), or null
   int gorder;      // tiled GEMM block order (set by its launcher): 0 row tiles fastest,
-                   // 1 XCD-grouped (row tiles per XCD, their position tiles adjacent)
+                   // 1 XCD-grouped (row tiles per XCD, their position tiles adjacent),
+                   // 2 one round in 2-D blocks per XCD (n_rt / 4 x n_tt / 2 tiles)
   int wnt;         // tiled GEMM: stage W rows by nontemporal loads (set by its launcher)
 };
 
