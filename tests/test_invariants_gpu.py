@@ -181,7 +181,7 @@ def test_build_segments_at_the_token_limit():
     assert np.array_equal(sr[:S].cpu().numpy(), np.array([c.adapters[a].rank if a >= 0 else 0 for a in o_sa]))
 
 
-@pytest.mark.parametrize("T", [1, 3, 64, 65, 130, 256, 511, 513, 1024, 1100, 3000])
+@pytest.mark.parametrize("T", [0, 1, 3, 64, 65, 130, 256, 511, 513, 1024, 1100, 3000])
 def test_build_segments_stable_grouping(T):
     # Canonical segmentation is a stable sort of the rows by id: ids ascending,
     # rows of one id in batch order, one segment per distinct id. Ids outside
@@ -203,6 +203,9 @@ def test_build_segments_stable_grouping(T):
     scale = (np.arange(cap, dtype=np.float32) + 1) / 8
     ti, ss, sa, sr, sc, ns = ml.build_segments(i32(ids), f32(scale), pool)
     torch.cuda.synchronize()
+    if T == 0:   # an empty batch: no segments, seg_start = [0]
+        assert int(ns.item()) == 0 and int(ss[0].item()) == 0
+        return
     order = np.argsort(ids, kind="stable")
     sid = ids[order]
     starts = np.flatnonzero(np.r_[True, sid[1:] != sid[:-1]])
