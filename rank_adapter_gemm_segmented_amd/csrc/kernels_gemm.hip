@@ -571,7 +571,10 @@ __global__ __launch_bounds__(256) void k_vfinal(LinearArgs a) {
 // are zero, so whole chunks are multiplied. The tiled GEMM adds delta to its
 // accumulators before the single rounding of y.
 // ---------------------------------------------------------------------------
-constexpr int kDxRows = 512;   // rows per workgroup
+// rows per workgroup: 256 (one pass of 256 / L rows per L-lane group at
+// rank <= 8, its smallest) took the heterogeneous LoRA-on call from 81.0 to
+// 78.7 us against 512, same bits; 1024 took it to 84.0 us
+constexpr int kDxRows = 256;
 
 template <int L>
 __device__ __forceinline__ void expand_rows(const LinearArgs& a, const uint16_t* bslot, int pitch, int n_base,
