@@ -571,15 +571,19 @@ __global__ __launch_bounds__(256) void k_vfinal(LinearArgs a) {
 // are zero, so whole chunks are multiplied. The tiled GEMM adds delta to its
 // accumulators before the single rounding of y.
 // ---------------------------------------------------------------------------
-// rows per workgroup: 256 (one pass of 256 / L rows per L-lane group at
-// rank <= 8, its smallest) took the heterogeneous LoRA-on call from 81.0 to
-// 78.7 us against 512, same bits; 1024 took it to 84.0 us
-constexpr int kDxRows = 256;
+// One wave per workgroup, 64 rows: on the heterogeneous batch the LoRA-on
+// call took 77.6 us, against 77.8 with 128 rows on 128 threads, 78.6 with 256
+// on 256, 81.0 with 512 on 256 and 84.0 with 1024 on 256 (same bits). Small
+// workgroups spread each position's rows over more CUs.
+constexpr int kDxRows = 64;      // rows per workgroup
+constexpr int kDxThreads = 64;   // threads per workgroup
+static_assert(kDxRows % kDxThreads == 0 && kDxThreads >= kDxMaxRank / 4,
+              "whole passes at every L; the threads that stage the v row exist");
 
 template <int L>
 __device__ __forceinline__ void expand_rows(const LinearArgs& a, const uint16_t* bslot, int pitch, int n_base,
                                             f32x4_t vq, bool vt, float* vs, float* __restrict__ drow) {
-  constexpr int RP = 256 / L;                        // rows per pass
+  constexpr int RP = kDxThreads / L;                 // rows per pass
   constexpr int NP = kDxRows / RP;                   // passes
   const int tid = threadIdx.x, c = tid % L, ro = tid / L;
   const bool c_ok = 8 * c < pitch;
@@ -612,7 +616,7 @@ __device__ __forceinline__ void expand_rows(const LinearArgs& a, const uint16_t*
   }
 }
 
-__global__ __launch_bounds__(256) void k_expand_delta(LinearArgs a) {
+__global__ __launch_bounds__(kDxThreads) void k_expand_delta(LinearArgs a) {
   __shared__ __attribute__((aligned(16))) float vs[kDxMaxRank];
   const int p = blockIdx.y, tid = threadIdx.x;
   const int n_base = blockIdx.x * kDxRows;
@@ -620,7 +624,7 @@ __global__ __launch_bounds__(256) void k_expand_delta(LinearArgs a) {
   const int4 pi = a.pos_info[p];
   const bool live = pi.y >= 0 && pi.y < a.pv.capacity && pi.z > 0;
   if (!live) {                                        // uniform: a zero term
-    for (int n = n_base + tid; n < min(n_base + kDxRows, a.d_out); n += 256) drow[n] = 0.f;
+    for (int n = n_base + tid; n < min(n_base + kDxRows, a.d_out); n += kDxThreads) drow[n] = 0.f;
     return;
   }
   const int r = min(min(pi.z, a.pv.max_rank), kDxMaxRank);
@@ -1376,7 +1380,7 @@ void launch_shrink_bf16(const LinearArgs& a, hipStream_t st) {
 void launch_linear_bf16(const LinearArgs& a, hipStream_t st) {
   launch_shrink_bf16(a, st);
   if (a.lora_on && a.delta && a.seg_grid > 0)
-    hipLaunchKernelGGL(k_expand_delta, dim3((a.d_out + kDxRows - 1) / kDxRows, a.T), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(k_expand_delta, dim3((a.d_out + kDxRows - 1) / kDxRows, a.T), dim3(kDxThreads), 0, st, a);
   auto tiles = [&](int br, int bt) {
     return (long long)((a.d_out + br - 1) / br) * ((a.T + bt - 1) / bt);
   };
