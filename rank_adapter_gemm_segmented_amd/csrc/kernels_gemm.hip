@@ -337,7 +337,8 @@ __global__ __launch_bounds__(256) void k_shrink2(LinearArgs a) {
 // through LDS in a fixed order (deterministic). Writes v_fin = scale * v and
 // the position table, as the one-chunk MFMA shrink does.
 // ---------------------------------------------------------------------------
-constexpr int kSsPos = 4;      // positions per item
+constexpr int kSsPos = 2;      // positions per item (a verify request's two tokens; 4 took the
+                               // verify LoRA-on call 0.6-0.9 us longer, 1 about 2 us longer)
 constexpr int kSsRows = 8;     // rank rows per workgroup (4 measured the same, 16 slower)
 constexpr int kSsMaxRank = 32; // largest pool rank it takes
 constexpr int kSsUnroll = 2;   // column groups per thread whose loads are in flight together
