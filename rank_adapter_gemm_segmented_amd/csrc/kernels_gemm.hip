@@ -533,14 +533,16 @@ __global__ __launch_bounds__(256) void k_vfinal(LinearArgs a) {
   const int q4 = a.r_ws / 4;
   if (e >= a.T * q4) return;
   const int p = e / q4, j = 4 * (e % q4);
+  // the chunk partials are requested together with the position entry (their
+  // addresses do not depend on it), not after it
+  f32x4_t part[kMaxShrinkSplit];
+#pragma unroll
+  for (int c = 0; c < kMaxShrinkSplit; ++c)
+    part[c] = *(const f32x4_t*)(a.v_part + ((long long)min(c, a.ks - 1) * a.T + p) * a.r_ws + j);
   const int4 pi = a.pos_info[p];
   const int rk = (pi.y >= 0 && pi.y < a.pv.capacity) ? min(pi.z, a.pv.max_rank) : 0;
   f32x4_t sum = f32x4_t{0.f, 0.f, 0.f, 0.f};
   if (j < rk) {
-    f32x4_t part[kMaxShrinkSplit];
-#pragma unroll
-    for (int c = 0; c < kMaxShrinkSplit; ++c)
-      part[c] = *(const f32x4_t*)(a.v_part + ((long long)min(c, a.ks - 1) * a.T + p) * a.r_ws + j);
 #pragma unroll
     for (int c = 0; c < kMaxShrinkSplit; ++c)
       if (c < a.ks) {
